@@ -1,0 +1,340 @@
+// CPU oracle for the VoxelBlockManager stencil pipeline.
+//
+// TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+// baseline of the benchmark may load this library.  It shares no code with the
+// HIP path: it rebuilds the index grid from the definitions, sweeps instead of
+// rank/select, and finds neighbours through a hash map from coordinate to
+// index.  Single-threaded; built with -O2 -ffp-contract=off and no fast-math so
+// every fp32 operation is one IEEE round-to-nearest-even step.
+//
+// Sources (the pages):
+//  * openvdb PR #2262 "NanoVDB VBM: Streaming box-stencil", section "What
+//    changed": in an index grid a stencil resolves to indices, index 0 means
+//    "no active voxel" and is skipped, a filter gathers sidecar[index*C + ch]
+//    and accumulates per channel, taps are visited in the order
+//    t = (di+1)*9 + (dj+1)*3 + (dk+1).
+//  * openvdb PR #2258 "VBM select-based inverse-map decode", sections
+//    "Summary" and "What changed": a block of BlockWidth slots; each slot's
+//    leaf is the block's first leaf plus the number of leaf starts (jumpMap
+//    bits) at or before it; the voxel is found through the leaf's 512-bit
+//    value mask and its 9-bit prefix-sum directory; the old decode swept all
+//    512 voxel slots of every leaf.  "Validation": final partial blocks and
+//    beyond-last-active sentinels.
+//  * openvdb PR #2263 "Alternative stencil resolvers for VoxelBlockManager",
+//    "Summary" (27-tap box and 7-tap cross shapes) and "Built on the
+//    register-decode API" (spanned leaves = 1 + popcount(jumpMap)).
+//
+// Readings where the pages leave a step open (each is listed in the design
+// notes of the repository):
+//  * leaves are 8^3 cells keyed by floor(p/8); voxel offset in a leaf is
+//    x-major: o = (x mod 8)*64 + (y mod 8)*8 + (z mod 8);
+//  * active indices are 1..N, assigned in tree order: root tile
+//    floor(p/4096) lexicographic (signed), then the 32^3 upper-node slot
+//    floor((p mod 4096)/128) x-major, then the 16^3 lower-node slot
+//    floor((p mod 128)/8) x-major, then the voxel offset o;
+//  * leafFirst of a leaf = index of its first active voxel;
+//  * prefix directory: one 64-bit word holding 7 fields of 9 bits, field k
+//    (bits 9k..9k+8) = number of active voxels in mask words 0..k;
+//  * block b covers indices 1+b*W .. min(N, (b+1)*W); firstLeafID = leaf of
+//    index 1+b*W; jumpMap bit s set iff slot s >= 1 holds an index that starts
+//    a new leaf;
+//  * decode sentinels: leafIndex 0xFFFFFFFF, voxelOffset 0xFFFF;
+//  * di runs along x, dj along y, dk along z;
+//  * cross taps: the box taps with |di|+|dj|+|dk| <= 1 in ascending box order;
+//  * box filter = plain sum (no division); cross sum = sum over 7 taps;
+//    7-point Laplacian = (sum of the active face taps, in cross order) minus
+//    the separately rounded product 6*centre.
+
+#include <algorithm>
+#include <array>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+namespace {
+
+int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) q -= 1;
+  return q;
+}
+int64_t floor_mod(int64_t a, int64_t b) { return a - b * floor_div(a, b); }
+
+struct Coord {
+  int64_t x, y, z;
+};
+
+// The 12 components that order active voxels: root tile, upper-node slot,
+// lower-node slot, voxel-in-leaf position; compared lexicographically.
+std::array<int64_t, 12> tree_order_key(const Coord& p) {
+  return {floor_div(p.x, 4096),        floor_div(p.y, 4096),        floor_div(p.z, 4096),
+          floor_mod(p.x, 4096) / 128,  floor_mod(p.y, 4096) / 128,  floor_mod(p.z, 4096) / 128,
+          floor_mod(p.x, 128) / 8,     floor_mod(p.y, 128) / 8,     floor_mod(p.z, 128) / 8,
+          floor_mod(p.x, 8),           floor_mod(p.y, 8),           floor_mod(p.z, 8)};
+}
+
+int voxel_offset_in_leaf(const Coord& p) {
+  return int(floor_mod(p.x, 8) * 64 + floor_mod(p.y, 8) * 8 + floor_mod(p.z, 8));
+}
+
+Coord leaf_origin_of(const Coord& p) {
+  return {8 * floor_div(p.x, 8), 8 * floor_div(p.y, 8), 8 * floor_div(p.z, 8)};
+}
+
+// coordinates are limited to |c| < 2^20, so three biased 21-bit fields pack a key
+uint64_t pack(const Coord& p) {
+  const int64_t bias = int64_t(1) << 20;
+  return (uint64_t(p.x + bias) << 42) | (uint64_t(p.y + bias) << 21) | uint64_t(p.z + bias);
+}
+
+struct Grid {
+  std::vector<Coord> voxel;                       // voxel[g-1] = coordinate of index g
+  std::unordered_map<uint64_t, uint64_t> index;   // coordinate -> index (absent = inactive)
+  std::vector<uint32_t> leaf_of;                  // leaf_of[g] for g = 1..N (entry 0 unused)
+  std::vector<Coord> leaf_origin;                 // per leaf, in leaf order
+  std::vector<uint64_t> leaf_first;               // per leaf: index of its first active voxel
+};
+
+// The 27 box offsets in tap order t = (di+1)*9 + (dj+1)*3 + (dk+1).
+Coord box_offset(int t) { return {t / 9 - 1, (t / 3) % 3 - 1, t % 3 - 1}; }
+
+// The cross: box taps with |di|+|dj|+|dk| <= 1, ascending.
+std::vector<int> cross_taps() {
+  std::vector<int> taps;
+  for (int t = 0; t < 27; ++t) {
+    Coord d = box_offset(t);
+    if (std::abs(d.x) + std::abs(d.y) + std::abs(d.z) <= 1) taps.push_back(t);
+  }
+  return taps;
+}
+
+uint64_t lookup(const Grid& g, const Coord& q) {
+  auto it = g.index.find(pack(q));
+  return it == g.index.end() ? 0 : it->second;
+}
+
+uint64_t tap_index(const Grid& g, uint64_t idx, int t) {
+  const Coord& p = g.voxel[idx - 1];
+  Coord d = box_offset(t);
+  return lookup(g, Coord{p.x + d.x, p.y + d.y, p.z + d.z});
+}
+
+int64_t n_blocks(int64_t n_active, int log2w) {
+  int64_t w = int64_t(1) << log2w;
+  return (n_active + w - 1) / w;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Builds the oracle's index grid from n coordinates (int32 x,y,z triples, any
+// order, duplicates allowed).  Returns NULL for a coordinate with |c| >= 2^20 - 1
+// (so that every neighbour coordinate still packs into three 21-bit fields).
+void* oracle_create(const int32_t* ijk, int64_t n) {
+  std::vector<Coord> pts;
+  pts.reserve(size_t(n));
+  for (int64_t i = 0; i < n; ++i) {
+    Coord p{ijk[3 * i], ijk[3 * i + 1], ijk[3 * i + 2]};
+    const int64_t lim = (int64_t(1) << 20) - 1;
+    if (p.x <= -lim || p.x >= lim || p.y <= -lim || p.y >= lim || p.z <= -lim || p.z >= lim) return nullptr;
+    pts.push_back(p);
+  }
+  std::vector<std::pair<std::array<int64_t, 12>, Coord>> keyed;
+  keyed.reserve(pts.size());
+  for (const Coord& p : pts) keyed.push_back({tree_order_key(p), p});
+  std::sort(keyed.begin(), keyed.end(),
+            [](const auto& a, const auto& b) { return a.first < b.first; });
+  keyed.erase(std::unique(keyed.begin(), keyed.end(),
+                          [](const auto& a, const auto& b) { return a.first == b.first; }),
+              keyed.end());
+
+  Grid* g = new (std::nothrow) Grid();
+  if (!g) return nullptr;
+  g->voxel.reserve(keyed.size());
+  g->leaf_of.assign(keyed.size() + 1, 0);
+  for (size_t i = 0; i < keyed.size(); ++i) {
+    const Coord& p = keyed[i].second;
+    uint64_t idx = uint64_t(i) + 1;
+    g->voxel.push_back(p);
+    g->index[pack(p)] = idx;
+    Coord o = leaf_origin_of(p);
+    bool new_leaf = g->leaf_origin.empty() || g->leaf_origin.back().x != o.x ||
+                    g->leaf_origin.back().y != o.y || g->leaf_origin.back().z != o.z;
+    if (new_leaf) {
+      g->leaf_origin.push_back(o);
+      g->leaf_first.push_back(idx);
+    }
+    g->leaf_of[idx] = uint32_t(g->leaf_origin.size() - 1);
+  }
+  return g;
+}
+
+void oracle_destroy(void* h) { delete static_cast<Grid*>(h); }
+
+int64_t oracle_n_active(const void* h) { return int64_t(static_cast<const Grid*>(h)->voxel.size()); }
+int64_t oracle_n_leaves(const void* h) { return int64_t(static_cast<const Grid*>(h)->leaf_origin.size()); }
+int64_t oracle_n_blocks(const void* h, int log2w) { return n_blocks(oracle_n_active(h), log2w); }
+
+// coords[(g-1)*3 + c] = coordinate c of index g, g = 1..N
+void oracle_voxels(const void* h, int32_t* coords) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  for (size_t i = 0; i < g.voxel.size(); ++i) {
+    coords[3 * i] = int32_t(g.voxel[i].x);
+    coords[3 * i + 1] = int32_t(g.voxel[i].y);
+    coords[3 * i + 2] = int32_t(g.voxel[i].z);
+  }
+}
+
+// Per leaf l (in leaf order): origin[3l..3l+2], mask[8l..8l+7] (bit o of the
+// 512-bit value mask is bit o%64 of word o/64), first[l], prefix[l].
+void oracle_leaves(const void* h, int32_t* origin, uint64_t* mask, uint64_t* first, uint64_t* prefix) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  const size_t L = g.leaf_origin.size();
+  std::vector<uint64_t> m(L * 8, 0);
+  for (size_t i = 0; i < g.voxel.size(); ++i) {
+    uint32_t l = g.leaf_of[i + 1];
+    int o = voxel_offset_in_leaf(g.voxel[i]);
+    m[l * 8 + size_t(o / 64)] |= uint64_t(1) << (o % 64);
+  }
+  for (size_t l = 0; l < L; ++l) {
+    origin[3 * l] = int32_t(g.leaf_origin[l].x);
+    origin[3 * l + 1] = int32_t(g.leaf_origin[l].y);
+    origin[3 * l + 2] = int32_t(g.leaf_origin[l].z);
+    first[l] = g.leaf_first[l];
+    uint64_t dir = 0, count = 0;
+    for (int w = 0; w < 8; ++w) {
+      mask[l * 8 + w] = m[l * 8 + w];
+      for (int b = 0; b < 64; ++b)
+        if ((m[l * 8 + w] >> b) & 1) ++count;
+      if (w < 7) dir |= count << (9 * w);
+    }
+    prefix[l] = dir;
+  }
+}
+
+// VBM block metadata for BlockWidth W = 2^log2w: first_leaf[b], and the W-bit
+// jumpMap of block b in words jump[b*(W/64) .. b*(W/64) + W/64 - 1].
+void oracle_blocks(const void* h, int log2w, uint32_t* first_leaf, uint64_t* jump) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  const int64_t N = int64_t(g.voxel.size());
+  const int64_t W = int64_t(1) << log2w;
+  const int64_t words = W / 64;
+  const int64_t nb = n_blocks(N, log2w);
+  for (int64_t b = 0; b < nb; ++b) {
+    first_leaf[b] = g.leaf_of[size_t(1 + b * W)];
+    for (int64_t k = 0; k < words; ++k) jump[b * words + k] = 0;
+    for (int64_t s = 1; s < W; ++s) {
+      int64_t idx = 1 + b * W + s;
+      if (idx <= N && g.leaf_of[size_t(idx)] != g.leaf_of[size_t(idx - 1)])
+        jump[b * words + s / 64] |= uint64_t(1) << (s % 64);
+    }
+  }
+}
+
+// Inverse maps by a sequential sweep over every leaf's 512 voxel positions:
+// slot (g-1) receives (leaf, offset) of index g; slots beyond N of the last
+// block receive the sentinels.  Arrays hold n_blocks*W entries.
+void oracle_decode(const void* h, int log2w, uint32_t* leaf_index, uint16_t* voxel_offset) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  const size_t L = g.leaf_origin.size();
+  std::vector<uint64_t> m(L * 8, 0);
+  for (size_t i = 0; i < g.voxel.size(); ++i) {
+    int o = voxel_offset_in_leaf(g.voxel[i]);
+    m[g.leaf_of[i + 1] * 8 + size_t(o / 64)] |= uint64_t(1) << (o % 64);
+  }
+  int64_t slot = 0;
+  for (size_t l = 0; l < L; ++l)
+    for (int o = 0; o < 512; ++o)
+      if ((m[l * 8 + size_t(o / 64)] >> (o % 64)) & 1) {
+        leaf_index[slot] = uint32_t(l);
+        voxel_offset[slot] = uint16_t(o);
+        ++slot;
+      }
+  const int64_t total = n_blocks(int64_t(g.voxel.size()), log2w) << log2w;
+  for (; slot < total; ++slot) {
+    leaf_index[slot] = 0xFFFFFFFFu;
+    voxel_offset[slot] = 0xFFFF;
+  }
+}
+
+// Raw stencil taps for the m indices in idx[]: taps[i*shape + j] = index of
+// tap j of voxel idx[i] (0 = inactive).  shape 27 = box, 7 = cross.
+int oracle_taps_rows(const void* h, int shape, const uint64_t* idx, int64_t m, uint64_t* taps) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  std::vector<int> order;
+  if (shape == 27) {
+    for (int t = 0; t < 27; ++t) order.push_back(t);
+  } else if (shape == 7) {
+    order = cross_taps();
+  } else {
+    return -1;
+  }
+  for (int64_t i = 0; i < m; ++i)
+    for (int j = 0; j < shape; ++j) taps[i * shape + j] = tap_index(g, idx[i], order[size_t(j)]);
+  return 0;
+}
+
+// Box filter for the m indices in idx[]: out[i*C + ch] = fp32 sum, in tap
+// order, of sidecar[tap*C + ch] over the active taps of voxel idx[i].
+void oracle_box_rows(const void* h, const float* sidecar, int C, const uint64_t* idx, int64_t m, float* out) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  for (int64_t i = 0; i < m; ++i) {
+    uint64_t tap[27];
+    for (int t = 0; t < 27; ++t) tap[t] = tap_index(g, idx[i], t);
+    for (int ch = 0; ch < C; ++ch) {
+      float acc = 0.0f;
+      for (int t = 0; t < 27; ++t)
+        if (tap[t]) acc += sidecar[tap[t] * uint64_t(C) + uint64_t(ch)];
+      out[i * C + ch] = acc;
+    }
+  }
+}
+
+// Cross filter for the m indices in idx[]; op 0 = sum of the 7 taps,
+// op 1 = 7-point Laplacian (sum of active faces) - fl(6 * centre).
+int oracle_cross_rows(const void* h, const float* sidecar, int C, int op, const uint64_t* idx, int64_t m,
+                      float* out) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  if (op != 0 && op != 1) return -1;
+  const std::vector<int> order = cross_taps();
+  for (int64_t i = 0; i < m; ++i) {
+    uint64_t tap[7];
+    for (int j = 0; j < 7; ++j) tap[j] = tap_index(g, idx[i], order[size_t(j)]);
+    for (int ch = 0; ch < C; ++ch) {
+      float acc = 0.0f;
+      for (int j = 0; j < 7; ++j) {
+        if (op == 1 && order[size_t(j)] == 13) continue;  // the centre enters only as -6*centre
+        if (tap[j]) acc += sidecar[tap[j] * uint64_t(C) + uint64_t(ch)];
+      }
+      if (op == 1) {
+        float six_centre = 6.0f * sidecar[idx[i] * uint64_t(C) + uint64_t(ch)];
+        acc = acc - six_centre;
+      }
+      out[i * C + ch] = acc;
+    }
+  }
+  return 0;
+}
+
+// Whole-grid filters: out has (N+1)*C floats; row 0 (index 0) is written as 0.
+void oracle_box_filter(const void* h, const float* sidecar, int C, float* out) {
+  const int64_t N = oracle_n_active(h);
+  for (int ch = 0; ch < C; ++ch) out[ch] = 0.0f;
+  std::vector<uint64_t> idx(static_cast<size_t>(N));
+  for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
+  oracle_box_rows(h, sidecar, C, idx.data(), N, out + C);
+}
+
+int oracle_cross_filter(const void* h, const float* sidecar, int C, int op, float* out) {
+  const int64_t N = oracle_n_active(h);
+  for (int ch = 0; ch < C; ++ch) out[ch] = 0.0f;
+  std::vector<uint64_t> idx(static_cast<size_t>(N));
+  for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
+  return oracle_cross_rows(h, sidecar, C, op, idx.data(), N, out + C);
+}
+
+}  // extern "C"
