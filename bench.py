@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the VBM stencil pipeline on one MI355X.
+
+Workload: the sphere shell of radius 185 and half thickness 1.5
+(1,290,538 active voxels, 11,255 leaves), interleaved fp32 sidecar with
+C = 16 channels, BlockWidth 128.  One step is one launch of the fused cached
+streaming 27-tap box filter: per slot decode, LDS neighbour-leaf table,
+streamed taps, gather-accumulate of 16 channels.
+
+The timed region holds exactly --steps launches back to back on the current
+stream, bracketed by torch.cuda.synchronize() and HIP events.  Inputs are
+resident in HBM; to keep the 256 MB Infinity Cache from serving repeated
+launches, successive steps rotate over several sidecar/output buffer sets
+whose total size exceeds three times the cache.
+
+Printed (stdout, one JSON line): value = active-voxel*channels per second,
+the roofline object for this kernel (algorithmic bytes per launch / mean
+launch time vs 8 TB/s), the CPU oracle baseline on the host, and extra
+measurements (other resolvers, channel counts, widths, the decode, the
+Laplacian) under "extra".  Progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes_filter(n_active, n_leaves, n_blocks, width, channels):
+    """Bytes a filter pass must move: own sidecar row read once, own output row
+    written once, leaf records (mask 64 + prefix 8 + first 8 + origin 12 B) and
+    block metadata (firstLeafID 4 B + jumpMap W/8 B)."""
+    return 8 * channels * n_active + 92 * n_leaves + (4 + width // 8) * n_blocks
+
+
+def alg_bytes_decode(n_active, n_leaves, n_blocks, width):
+    """Decode: 6 B written per slot (u32 + u16), leaf mask/prefix/first (80 B),
+    block metadata."""
+    return 6 * n_blocks * width + 80 * n_leaves + (4 + width // 8) * n_blocks
+
+
+def time_launches(fn, n_sets, steps, warmup):
+    """Mean ms per launch of fn(k) for k = 0..steps-1 over rotating buffer sets."""
+    import torch
+    for k in range(warmup):
+        fn(k % n_sets)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        fn(k % n_sets)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--channels", type=int, default=16)
+    ap.add_argument("--log2w", type=int, default=7)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="profile mode: run only this variant (e.g. box_cs) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the VBM pipeline here is a single-GPU build "
+              "(see the sharding note in DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from nanovdb_stencil_filtering_amd import inputs, vbm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    vbm.load_library()
+    C = args.channels
+    log("bench: generating cfg-shell")
+    coords = inputs.shell_coords(**inputs.CFG_SHELL)
+    grids = {w: vbm.build(coords, w, device=dev) for w in sorted({args.log2w, 7, 9})}
+    g = grids[args.log2w]
+    N, L, nb, W = g.n_active, g.n_leaves, g.n_blocks, g.width
+    log("bench: N=%d leaves=%d blocks=%d W=%d C=%d" % (N, L, nb, W, C))
+
+    def make_sets(channels):
+        sc = torch.from_numpy(inputs.sidecar(2, N, channels)).to(dev)
+        per_set = 2 * sc.numel() * 4
+        n_sets = max(2, -(-3 * MALL_BYTES // per_set))
+        scs = [sc] + [sc.clone() for _ in range(n_sets - 1)]
+        outs = [torch.empty_like(sc) for _ in range(n_sets)]
+        return scs, outs, n_sets
+
+    scs, outs, n_sets = make_sets(C)
+    flags_cs = vbm.CACHED | vbm.STREAMING
+
+    def box_step(grid, flags, scs_, outs_):
+        return lambda k: vbm.box_filter(grid, scs_[k], flags, out=outs_[k])
+
+    if args.only:
+        # profiling mode: one variant, plain launches, no CPU leg
+        variants = {"box_cs": flags_cs, "box_c": vbm.CACHED, "box_s": vbm.STREAMING, "box_p": 0}
+        fn = box_step(g, variants[args.only], scs, outs)
+        ms = time_launches(fn, n_sets, args.steps, args.warmup)
+        log("only %s: %.4f ms/launch" % (args.only, ms))
+        return
+
+    # sanity: the headline variant equals the plain materialised one, bit for bit
+    a = vbm.box_filter(g, scs[0], flags_cs)
+    b = vbm.box_filter(g, scs[0], 0)
+    torch.cuda.synchronize()
+    if not torch.equal(a.view(torch.int32), b.view(torch.int32)):
+        raise SystemExit("bench: cached streaming and plain materialised outputs differ")
+
+    log("bench: timing %d steps (warmup %d), %d rotating buffer sets" % (args.steps, args.warmup, n_sets))
+    torch.cuda.synchronize()
+    ms = time_launches(box_step(g, flags_cs, scs, outs), n_sets, args.steps, args.warmup)
+    value = N * C / (ms * 1e-3)
+    ab = alg_bytes_filter(N, L, nb, W, C)
+    achieved = ab / (ms * 1e-3) / 1e9
+    log("bench: headline %.4f ms/step, %.3e voxel*ch/s, %.1f GB/s" % (ms, value, achieved))
+
+    extra = {}
+    if not args.no_extra:
+        def rec(name, ms_, bytes_, n_work=None):
+            d = {"ms": round(ms_, 5), "GBps": round(bytes_ / (ms_ * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(bytes_ / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if n_work is not None:
+                d["voxel_ch_per_s"] = float("%.4e" % (n_work / (ms_ * 1e-3)))
+            extra[name] = d
+            log("  %-34s %.4f ms  %7.1f GB/s" % (name, ms_, d["GBps"]))
+
+        names = {0: "plain_materialised", vbm.STREAMING: "plain_streaming", vbm.CACHED: "cached_materialised",
+                 flags_cs: "cached_streaming"}
+        for ch in sorted({1, 3, 8, 16}):
+            s_, o_, ns_ = (scs, outs, n_sets) if ch == C else make_sets(ch)
+            for w in (7, 9):
+                gw = grids[w]
+                for fl, nm in names.items():
+                    t = time_launches(box_step(gw, fl, s_, o_), ns_, 20, 5)
+                    rec("box_%s_W%d_C%d" % (nm, gw.width, ch), t,
+                        alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch), N * ch)
+            for w in (7, 9):
+                gw = grids[w]
+                if ch in (1, 8):
+                    for cached in (0, vbm.CACHED):
+                        t = time_launches(lambda k: vbm.cross_filter(gw, s_[k], cached | vbm.OP_LAPLACIAN,
+                                                                     out=o_[k]), ns_, 20, 5)
+                        rec("laplacian_%s_W%d_C%d" % ("cached" if cached else "plain", gw.width, ch), t,
+                            alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch), N * ch)
+            if ch != C:
+                del s_, o_
+        # hot-cache figure (single buffer set; the Infinity Cache may serve it)
+        t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
+        rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
+        for w in (7, 9):
+            gw = grids[w]
+            lo = [torch.empty(gw.n_slots, dtype=torch.int32, device=dev) for _ in range(4)]
+            oo = [torch.empty(gw.n_slots, dtype=torch.int16, device=dev) for _ in range(4)]
+            lib = vbm.load_library()
+            import ctypes
+
+            def dec(k, gw=gw, lo=lo, oo=oo):
+                rc = lib.vbm_decode(ctypes.byref(gw.hdr), ctypes.c_void_p(gw.blob.data_ptr()),
+                                    ctypes.c_void_p(lo[k].data_ptr()), ctypes.c_void_p(oo[k].data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                assert rc == 0
+            t = time_launches(dec, 4, 50, 15)
+            rec("decode_W%d" % gw.width, t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        log("bench: CPU oracle baseline")
+        ref = oracle.OracleGrid(coords)
+        sc_host = inputs.sidecar(2, N, C)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and reps < 20:
+            t0 = time.perf_counter()
+            ref.box(sc_host)
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": float("%.4e" % (N * C * reps / t_cpu)), "unit": "active-voxel*channels/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "whole cfg-shell box filter (C=%d, N=%d), %d passes, %.1f s, single thread" %
+                         (C, N, reps, t_cpu)}
+        log("bench: oracle %.3e voxel*ch/s" % cpu["value"])
+
+    out = {
+        "metric": "box-filter active-voxel*channels/s (cached streaming 27-tap box, C=%d)" % C,
+        "value": float("%.6e" % value),
+        "unit": "active-voxel*channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sphere shell R=185 |d|<=1.5, N=%d, leaves=%d, BlockWidth %d, C=%d fp32 sidecar, "
+                               "cached streaming box filter" % (N, L, W, C),
+                   "n_active": N, "n_leaves": L, "block_width": W, "channels": C,
+                   "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": ab, "kernel": "k_box<16,true,true,true>"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * vbm.h -- C ABI of the MI355X (gfx950) VoxelBlockManager stencil pipeline.
+ *
+ * An index grid maps each active voxel of a sparse set to an index 1..N
+ * (0 = inactive).  A VoxelBlockManager (VBM) cuts the indices into blocks of
+ * BlockWidth = 2^log2_width consecutive slots; per block it keeps the first
+ * leaf and a jumpMap bit per slot that starts a new leaf.  On that structure
+ * the library runs the stencil pipeline on the GPU:
+ *   decode    slot -> (leafIndex, voxelOffset) by rank into the jumpMap and
+ *             select into the leaf's value mask through its prefix directory
+ *             (openvdb PR #2258, "VBM select-based inverse-map decode",
+ *             "Summary" and "What changed");
+ *   resolve   the 27-tap box and 7-tap cross stencils to indices, by a
+ *             root-down tree walk per tap or through a per-block table of
+ *             neighbour leaves staged in LDS (openvdb PR #2263, "Alternative
+ *             stencil resolvers for VoxelBlockManager", "Summary");
+ *   deliver   taps materialised into an array or streamed to the consumer in
+ *             tap order t = (di+1)*9 + (dj+1)*3 + (dk+1)
+ *             (openvdb PR #2262, "NanoVDB VBM: Streaming box-stencil",
+ *             "What changed");
+ *   gather    per channel, the fp32 sum over the active taps of
+ *             sidecar[index*C + ch] (same section of PR #2262).
+ *
+ * Conventions for every entry point
+ *   - Return 0 (VBM_OK) or a negative vbm_status.  Nothing throws.
+ *   - Arguments are validated before any HIP call; on a validation error no
+ *     work is enqueued and no output is touched.
+ *   - GPU work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  Nothing synchronises.  A failed
+ *     launch is reported as VBM_ERR_HIP.
+ *   - Device buffers are owned by the caller.  The library allocates no device
+ *     memory and keeps no state between calls.
+ *   - Coordinates x -> di, y -> dj, z -> dk.  Leaves are 8^3; the voxel offset
+ *     inside a leaf is o = (x&7)*64 + (y&7)*8 + (z&7).
+ */
+#ifndef VBM_H
+#define VBM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vbm_status {
+  VBM_OK = 0,
+  VBM_ERR_ARG = -1,         /* null pointer, bad width / C / shape / flags, corrupt grid header */
+  VBM_ERR_SIZE = -2,        /* grid too large for the library's index or memory limits          */
+  VBM_ERR_ALIGN = -3,       /* float buffer not 4-byte aligned                                 */
+  VBM_ERR_ALIAS = -4,       /* output overlaps the sidecar (neighbours are read while writing) */
+  VBM_ERR_RANGE = -5,       /* coordinate with |c| >= 2^30                                      */
+  VBM_ERR_HIP = -6,         /* a HIP launch failed                                              */
+  VBM_ERR_UNSUPPORTED = -7, /* a combination the library does not offer                         */
+  VBM_ERR_NOMEM = -8        /* host allocation in vbm_build failed                              */
+} vbm_status;
+
+/* flags */
+#define VBM_CACHED 0x1        /* resolve through the LDS neighbour-leaf table (else tree walk)  */
+#define VBM_STREAMING 0x2     /* box only: stream taps to the consumer (else materialise 27)   */
+#define VBM_OP_SUM 0x0        /* cross filter: sum of the 7 taps                                */
+#define VBM_OP_LAPLACIAN 0x4  /* cross filter: (sum of active faces) - 6*centre                 */
+
+#define VBM_MAX_CACHED_LEAVES 16  /* openvdb PR #2263, "Notes": MaxCachedLeaves is 16           */
+#define VBM_GRID_MAGIC 0x314D4256u /* "VBM1" */
+
+/*
+ * Host-side description of a built grid.  Filled by vbm_build and passed by
+ * pointer to every GPU call together with the device copy of the blob.  All
+ * offsets are byte offsets into the blob; every section starts 256-byte
+ * aligned.  Blob sections:
+ *   leaves            n_leaves records of 128 bytes:
+ *                       u64 mask[8]   512-bit value mask, bit o = bit o%64 of word o/64
+ *                       u64 prefix    7 fields of 9 bits: field k (bits 9k..9k+8) =
+ *                                     active voxels in mask words 0..k
+ *                       u64 first     index of the leaf's first active voxel
+ *                       i32 origin[3] leaf min corner
+ *                       36 bytes of zero padding
+ *   root              n_root tiles of 16 bytes: i32 key[3] (= origin >> 12), u32 upper node;
+ *                     sorted by key, lexicographic, signed
+ *   upper             n_upper nodes of 32768 u32: lower-node id or 0xFFFFFFFF, slot
+ *                     ((x>>7)&31)<<10 | ((y>>7)&31)<<5 | ((z>>7)&31)
+ *   lower             n_lower nodes of 4096 u32: leaf id or 0xFFFFFFFF, slot
+ *                     ((x>>3)&15)<<8 | ((y>>3)&15)<<4 | ((z>>3)&15)
+ *   block_first_leaf  n_blocks u32: leaf owning slot 0 of the block
+ *   block_jump        n_blocks * (W/64) u64: jumpMap; bit s set iff slot s >= 1 holds an
+ *                     index that starts a leaf
+ * Indices follow tree order: root tile, upper slot, lower slot, voxel offset.
+ */
+typedef struct vbm_grid {
+  uint32_t magic;          /* VBM_GRID_MAGIC                                      */
+  int32_t log2_width;      /* BlockWidth W = 1 << log2_width, 6..9                */
+  uint64_t n_active;       /* N: active voxels; indices are 1..N, 0 = inactive    */
+  uint32_t n_leaves;
+  uint32_t n_blocks;       /* ceil(N / W)                                         */
+  uint32_t n_root;
+  uint32_t n_upper;
+  uint32_t n_lower;
+  uint32_t reserved;
+  uint64_t blob_bytes;
+  uint64_t off_leaves;
+  uint64_t off_root;
+  uint64_t off_upper;
+  uint64_t off_lower;
+  uint64_t off_block_first_leaf;
+  uint64_t off_block_jump;
+} vbm_grid;
+
+/*
+ * Build an index grid and its VBM metadata on the host (not on the timed path).
+ *   ijk        host int32 [n][3] coordinates, any order; duplicates are collapsed
+ *              (the input is a set).  May be NULL when n == 0.
+ *   n          number of coordinates (>= 0)
+ *   log2_width 6..9 (BlockWidth 64..512; openvdb PR #2258, "A/B" table)
+ *   grid       out: header
+ *   host_blob  out: *host_blob = a blob of grid->blob_bytes bytes allocated by the
+ *              library; the caller copies it to the device and releases it with
+ *              vbm_free_blob.
+ * Errors: VBM_ERR_ARG (null pointers, bad width, n < 0), VBM_ERR_RANGE
+ * (|coordinate| >= 2^30), VBM_ERR_SIZE (more than 2^32 - 2 active voxels),
+ * VBM_ERR_NOMEM.  On error *host_blob is NULL.
+ */
+int vbm_build(const int32_t* ijk, int64_t n, int log2_width, vbm_grid* grid, void** host_blob);
+
+/* Release a blob returned by vbm_build.  NULL is ignored. */
+void vbm_free_blob(void* host_blob);
+
+/*
+ * Inverse-map decode of every slot (openvdb PR #2258, "What changed": rank of
+ * the slot into the block's jumpMap picks the leaf; the prefix directory picks
+ * the 64-bit mask word; an in-word select recovers the voxel offset).
+ *   d_blob          device copy of the blob
+ *   d_leaf_index    device u32 [n_blocks * W]: leaf of slot s of block b at b*W + s
+ *   d_voxel_offset  device u16 [n_blocks * W]: voxel offset o in that leaf
+ * Slots past the last active index (the final partial block) receive the
+ * sentinels 0xFFFFFFFF and 0xFFFF (openvdb PR #2258, "Validation").
+ * Errors: VBM_ERR_ARG, VBM_ERR_HIP.
+ */
+int vbm_decode(const vbm_grid* grid, const void* d_blob, uint32_t* d_leaf_index, uint16_t* d_voxel_offset,
+               void* stream);
+
+/*
+ * Raw stencil taps of every slot (openvdb PR #2263, "Validation": all taps of
+ * every thread written to global memory and compared bytewise).
+ *   shape   27 (box, tap t = (di+1)*9 + (dj+1)*3 + (dk+1)) or 7 (cross: the box
+ *           taps 4, 10, 12, 13, 14, 16, 22, i.e. -x, -y, -z, centre, +z, +y, +x)
+ *   flags   VBM_CACHED and, for the box, VBM_STREAMING (taps are then written from
+ *           the streaming callback instead of a materialised array)
+ *   d_taps  device u64 [n_blocks * W * shape]: row b*W + s = taps of slot s of block b;
+ *           0 = inactive neighbour; rows of sentinel slots are all 0
+ * Errors: VBM_ERR_ARG, VBM_ERR_UNSUPPORTED (cross with VBM_STREAMING:
+ * openvdb PR #2263, "Notes", has no streaming cross form), VBM_ERR_HIP.
+ */
+int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int shape, int flags, uint64_t* d_taps,
+                        void* stream);
+
+/*
+ * 27-tap box filter (openvdb PR #2262, "What changed" and "A/B"):
+ *   out[g*C + ch] = fp32 sum, in tap order from +0, of sidecar[tap*C + ch] over
+ *   the active taps of voxel g (no division).  Row 0 of out is written as 0.
+ *   d_sidecar  device f32 [(N+1) * C], row g = channels of index g (row 0 unused)
+ *   d_out      device f32 [(N+1) * C]; must not overlap d_sidecar
+ *   C          channels >= 1
+ *   flags      VBM_CACHED | VBM_STREAMING in any combination (the four resolvers of
+ *              openvdb PR #2263, "Summary" table)
+ * All four variants give bit-identical outputs.
+ * Errors: VBM_ERR_ARG, VBM_ERR_ALIGN, VBM_ERR_ALIAS, VBM_ERR_HIP.
+ */
+int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                   int flags, void* stream);
+
+/*
+ * 7-tap cross filter (openvdb PR #2263, "Measurements": cross variants
+ * accumulate their 7 taps; openvdb PR #2258, "A/B": the 7-point Laplacian):
+ *   VBM_OP_SUM        out = fp32 sum, in cross order from +0, over the active taps
+ *   VBM_OP_LAPLACIAN  out = (fp32 sum over the active face taps in cross order)
+ *                           - fl(6 * centre)
+ *   flags: VBM_CACHED plus one op.  Taps are materialised (7 entries).
+ * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
+ * VBM_ERR_ALIAS, VBM_ERR_UNSUPPORTED (VBM_STREAMING), VBM_ERR_HIP.
+ */
+int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                     int flags, void* stream);
+
+/* Static English text for a status code. */
+const char* vbm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VBM_H */

@@ -23,6 +23,8 @@ published 64-bit finaliser.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -185,8 +187,7 @@ def value_noise(seed: int, p: np.ndarray, wavelengths=(128.0, 64.0, 32.0),
     values interpolated trilinearly with smoothstep weights, summed with
     amplitudes total_amplitude * (4, 2, 1) / 7 for three octaves."""
     if amplitudes is None:
-        w = np.array([2.0 ** (len(wavelengths) - 1 - i) for i in range(len(wavelengths))])
-        amplitudes = total_amplitude * w / w.sum()
+        amplitudes = _octave_amplitudes(len(wavelengths), total_amplitude)
     n = np.zeros(p.shape[0], dtype=np.float64)
     for o, (lam, amp) in enumerate(zip(wavelengths, amplitudes)):
         u = p / lam
@@ -205,20 +206,61 @@ def value_noise(seed: int, p: np.ndarray, wavelengths=(128.0, 64.0, 32.0),
     return n
 
 
-def band_coords(seed: int, radius: float = 600.0, half_width: float = 3.0,
-                amplitude: float = 20.0) -> np.ndarray:
-    """Narrow band |d(p)| <= half_width with d(p) = ||p|| - (radius + noise(p)),
-    noise = 3-octave value noise of total amplitude ``amplitude``."""
+def _octave_amplitudes(n_octaves: int, total_amplitude: float):
+    w = np.array([2.0 ** (n_octaves - 1 - i) for i in range(n_octaves)])
+    return total_amplitude * w / w.sum()
+
+
+class _LatticeNoise:
+    """value_noise with each octave's lattice values tabulated once over a box.
+
+    Same lattice values and the same float64 operations in the same order as
+    ``value_noise``, so the results are identical (a CPU test checks this)."""
+
+    def __init__(self, seed, lo, hi, wavelengths=(128.0, 64.0, 32.0), total_amplitude=20.0):
+        self.wavelengths = wavelengths
+        self.amplitudes = _octave_amplitudes(len(wavelengths), total_amplitude)
+        self.tables = []
+        for o, lam in enumerate(wavelengths):
+            i_lo = int(np.floor(lo / lam)) - 1
+            i_hi = int(np.floor(hi / lam)) + 2
+            ax = np.arange(i_lo, i_hi + 1, dtype=np.int64)
+            ix, iy, iz = np.meshgrid(ax, ax, ax, indexing="ij")
+            vals = _lattice_values(seed, o, ix.ravel(), iy.ravel(), iz.ravel()).reshape(ix.shape)
+            self.tables.append((i_lo, vals))
+
+    def __call__(self, p):
+        n = np.zeros(p.shape[0], dtype=np.float64)
+        for (lam, amp, (i_lo, tab)) in zip(self.wavelengths, self.amplitudes, self.tables):
+            u = p / lam
+            i0 = np.floor(u).astype(np.int64)
+            f = u - i0
+            s = f * f * (3.0 - 2.0 * f)
+            j = i0 - i_lo
+            acc = np.zeros(p.shape[0], dtype=np.float64)
+            for cx in (0, 1):
+                wx = s[:, 0] if cx else 1.0 - s[:, 0]
+                for cy in (0, 1):
+                    wy = s[:, 1] if cy else 1.0 - s[:, 1]
+                    for cz in (0, 1):
+                        wz = s[:, 2] if cz else 1.0 - s[:, 2]
+                        acc += wx * wy * wz * tab[j[:, 0] + cx, j[:, 1] + cy, j[:, 2] + cz]
+            n += amp * acc
+        return n
+
+
+def _band_slab(args):
+    seed, radius, half_width, amplitude, xs = args
     reach = amplitude + half_width
-    r_in = radius - reach
-    r_out = radius + reach
+    r_in, r_out = radius - reach, radius + reach
     ext = int(np.ceil(r_out))
+    noise = _LatticeNoise(seed, -ext, ext, total_amplitude=amplitude)
     ax = np.arange(-ext, ext + 1, dtype=np.int64)
-    out = []
     yy, zz = np.meshgrid(ax, ax, indexing="ij")
     y_flat, z_flat = yy.ravel(), zz.ravel()
     yz2 = y_flat * y_flat + z_flat * z_flat
-    for x in ax:
+    out = []
+    for x in xs:
         r2 = yz2 + x * x
         cand = np.nonzero((r2 >= r_in * r_in) & (r2 <= r_out * r_out))[0]
         if cand.size == 0:
@@ -227,11 +269,34 @@ def band_coords(seed: int, radius: float = 600.0, half_width: float = 3.0,
         p[:, 0] = x
         p[:, 1] = y_flat[cand]
         p[:, 2] = z_flat[cand]
-        d = np.sqrt(r2[cand].astype(np.float64)) - (radius + value_noise(seed, p, total_amplitude=amplitude))
+        d = np.sqrt(r2[cand].astype(np.float64)) - (radius + noise(p))
         keep = np.abs(d) <= half_width
         if keep.any():
             out.append(p[keep].astype(np.int32))
     return np.concatenate(out, axis=0) if out else np.zeros((0, 3), np.int32)
+
+
+def band_coords(seed: int, radius: float = 600.0, half_width: float = 3.0,
+                amplitude: float = 20.0, workers: int | None = None) -> np.ndarray:
+    """Narrow band |d(p)| <= half_width with d(p) = ||p|| - (radius + noise(p)),
+    noise = 3-octave value noise of total amplitude ``amplitude`` (wavelengths
+    128, 64, 32; amplitudes in ratio 4:2:1).  Slabs of constant x are
+    evaluated in parallel processes; the result is in x-major order."""
+    import multiprocessing as mp
+    ext = int(np.ceil(radius + amplitude + half_width))
+    xs = np.arange(-ext, ext + 1, dtype=np.int64)
+    if workers is None:
+        workers = max(1, min(16, (os.cpu_count() or 1)))
+    n_chunks = max(1, workers * 4)
+    bounds = np.linspace(0, xs.size, n_chunks + 1).astype(int)
+    chunks = [xs[bounds[i]:bounds[i + 1]] for i in range(n_chunks) if bounds[i + 1] > bounds[i]]
+    args = [(seed, radius, half_width, amplitude, c) for c in chunks]
+    if workers == 1:
+        parts = [_band_slab(a) for a in args]
+    else:
+        with mp.get_context("fork").Pool(workers) as pool:
+            parts = pool.map(_band_slab, args)
+    return np.concatenate(parts, axis=0)
 
 
 def shuffled(coords: np.ndarray, seed: int) -> np.ndarray:

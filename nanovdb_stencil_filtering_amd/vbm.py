@@ -1,0 +1,246 @@
+"""Python binding of libvbm.so (the C ABI in include/vbm.h).
+
+Argument marshalling only: every step of the stencil pipeline runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current
+stream.  The names mirror the C entry points:
+
+    build(coords, log2_width)          vbm_build  (host) + copy of the blob to the GPU
+    decode(grid)                       vbm_decode
+    stencil_indices(grid, shape, ...)  vbm_stencil_indices
+    box_filter(grid, sidecar, ...)     vbm_box_filter
+    cross_filter(grid, sidecar, ...)   vbm_cross_filter
+
+There is no CPU fallback: if the library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libvbm.so")
+
+CACHED = 0x1
+STREAMING = 0x2
+OP_SUM = 0x0
+OP_LAPLACIAN = 0x4
+MAX_CACHED_LEAVES = 16
+GRID_MAGIC = 0x314D4256
+
+STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN", -4: "VBM_ERR_ALIAS",
+          -5: "VBM_ERR_RANGE", -6: "VBM_ERR_HIP", -7: "VBM_ERR_UNSUPPORTED", -8: "VBM_ERR_NOMEM"}
+
+EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_decode", "vbm_stencil_indices", "vbm_box_filter",
+            "vbm_cross_filter", "vbm_strerror")
+
+
+class VbmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, str(status)), _strerror(status)))
+
+
+class GridHeader(ctypes.Structure):
+    """Mirror of struct vbm_grid."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("log2_width", ctypes.c_int32), ("n_active", ctypes.c_uint64),
+        ("n_leaves", ctypes.c_uint32), ("n_blocks", ctypes.c_uint32), ("n_root", ctypes.c_uint32),
+        ("n_upper", ctypes.c_uint32), ("n_lower", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("blob_bytes", ctypes.c_uint64), ("off_leaves", ctypes.c_uint64), ("off_root", ctypes.c_uint64),
+        ("off_upper", ctypes.c_uint64), ("off_lower", ctypes.c_uint64),
+        ("off_block_first_leaf", ctypes.c_uint64), ("off_block_jump", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libvbm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libvbm.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m nanovdb_stencil_filtering_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    GP = ctypes.POINTER(GridHeader)
+    lib.vbm_build.restype = I
+    lib.vbm_build.argtypes = [P, I64, I, GP, ctypes.POINTER(ctypes.c_void_p)]
+    lib.vbm_free_blob.restype = None
+    lib.vbm_free_blob.argtypes = [P]
+    lib.vbm_decode.restype = I
+    lib.vbm_decode.argtypes = [GP, P, P, P, P]
+    lib.vbm_stencil_indices.restype = I
+    lib.vbm_stencil_indices.argtypes = [GP, P, I, I, P, P]
+    lib.vbm_box_filter.restype = I
+    lib.vbm_box_filter.argtypes = [GP, P, P, P, I, I, P]
+    lib.vbm_cross_filter.restype = I
+    lib.vbm_cross_filter.argtypes = [GP, P, P, P, I, I, P]
+    lib.vbm_strerror.restype = ctypes.c_char_p
+    lib.vbm_strerror.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+def _strerror(status: int) -> str:
+    try:
+        return load_library().vbm_strerror(status).decode()
+    except Exception:  # pragma: no cover - library missing while formatting an error
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise VbmError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# host build
+# ---------------------------------------------------------------------------
+
+def build_host(coords: np.ndarray, log2_width: int):
+    """vbm_build: returns (header, blob as a numpy uint8 array owned by Python)."""
+    lib = load_library()
+    c = np.ascontiguousarray(coords, dtype=np.int32).reshape(-1, 3)
+    hdr = GridHeader()
+    blob = ctypes.c_void_p()
+    ptr = c.ctypes.data_as(ctypes.c_void_p) if c.size else None
+    _check(lib.vbm_build(ptr, c.shape[0], int(log2_width), ctypes.byref(hdr), ctypes.byref(blob)), "vbm_build")
+    try:
+        host = np.ctypeslib.as_array(ctypes.cast(blob, ctypes.POINTER(ctypes.c_uint8)),
+                                     shape=(hdr.blob_bytes,)).copy()
+    finally:
+        lib.vbm_free_blob(blob)
+    return hdr, host
+
+
+def blob_sections(hdr: GridHeader, blob: np.ndarray) -> dict:
+    """Numpy views of the blob's sections (layout of include/vbm.h)."""
+    L, nb, W = hdr.n_leaves, hdr.n_blocks, 1 << hdr.log2_width
+    leaf_dt = np.dtype([("mask", "<u8", (8,)), ("prefix", "<u8"), ("first", "<u8"), ("origin", "<i4", (3,)),
+                        ("pad", "<u4", (9,))])
+    root_dt = np.dtype([("key", "<i4", (3,)), ("upper", "<u4")])
+
+    def sec(off, dt, count):
+        return np.frombuffer(blob, dtype=dt, count=count, offset=off)
+
+    return dict(
+        leaves=sec(hdr.off_leaves, leaf_dt, L),
+        root=sec(hdr.off_root, root_dt, hdr.n_root),
+        upper=sec(hdr.off_upper, "<u4", hdr.n_upper * 32768).reshape(hdr.n_upper, 32768),
+        lower=sec(hdr.off_lower, "<u4", hdr.n_lower * 4096).reshape(hdr.n_lower, 4096),
+        block_first_leaf=sec(hdr.off_block_first_leaf, "<u4", nb),
+        block_jump=sec(hdr.off_block_jump, "<u8", nb * (W // 64)).reshape(nb, W // 64),
+    )
+
+
+# ---------------------------------------------------------------------------
+# device side
+# ---------------------------------------------------------------------------
+
+class Grid:
+    """A built grid: its header and the blob resident in device memory."""
+
+    def __init__(self, hdr: GridHeader, blob):
+        self.hdr = hdr
+        self.blob = blob  # torch.uint8 tensor on the device
+
+    @property
+    def n_active(self) -> int:
+        return int(self.hdr.n_active)
+
+    @property
+    def n_leaves(self) -> int:
+        return int(self.hdr.n_leaves)
+
+    @property
+    def n_blocks(self) -> int:
+        return int(self.hdr.n_blocks)
+
+    @property
+    def log2_width(self) -> int:
+        return int(self.hdr.log2_width)
+
+    @property
+    def width(self) -> int:
+        return 1 << int(self.hdr.log2_width)
+
+    @property
+    def n_slots(self) -> int:
+        return self.n_blocks * self.width
+
+
+def build(coords: np.ndarray, log2_width: int, device="cuda") -> Grid:
+    import torch
+    hdr, host = build_host(coords, log2_width)
+    blob = torch.from_numpy(host).to(device)
+    return Grid(hdr, blob)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _blob_ptr(grid: Grid):
+    return _ptr(grid.blob)
+
+
+def decode(grid: Grid, stream=None):
+    """vbm_decode -> (leafIndex as int32 tensor, voxelOffset as int16 tensor), n_blocks*W each
+    (bit patterns of u32 / u16)."""
+    import torch
+    dev = grid.blob.device
+    leaf = torch.empty(grid.n_slots, dtype=torch.int32, device=dev)
+    off = torch.empty(grid.n_slots, dtype=torch.int16, device=dev)
+    _check(load_library().vbm_decode(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(leaf), _ptr(off),
+                                     _stream_ptr(stream)), "vbm_decode")
+    return leaf, off
+
+
+def stencil_indices(grid: Grid, shape: int, flags: int = 0, stream=None):
+    """vbm_stencil_indices -> int64 tensor [n_blocks*W, shape] (u64 bit patterns)."""
+    import torch
+    taps = torch.empty((grid.n_slots, shape), dtype=torch.int64, device=grid.blob.device)
+    _check(load_library().vbm_stencil_indices(ctypes.byref(grid.hdr), _blob_ptr(grid), int(shape), int(flags),
+                                              _ptr(taps), _stream_ptr(stream)), "vbm_stencil_indices")
+    return taps
+
+
+def _filter_out(grid: Grid, sidecar, out):
+    import torch
+    if sidecar.dtype != torch.float32 or sidecar.dim() != 2 or sidecar.shape[0] != grid.n_active + 1:
+        raise ValueError("sidecar must be float32 [(N+1), C]")
+    if not sidecar.is_contiguous():
+        raise ValueError("sidecar must be contiguous")
+    if out is None:
+        out = torch.empty_like(sidecar)
+    elif out.shape != sidecar.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like the sidecar")
+    return out
+
+
+def box_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, stream=None):
+    """vbm_box_filter -> out float32 [(N+1), C]."""
+    out = _filter_out(grid, sidecar, out)
+    _check(load_library().vbm_box_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
+                                         int(sidecar.shape[1]), int(flags), _stream_ptr(stream)), "vbm_box_filter")
+    return out
+
+
+def cross_filter(grid: Grid, sidecar, flags: int = CACHED | OP_SUM, out=None, stream=None):
+    """vbm_cross_filter -> out float32 [(N+1), C]."""
+    out = _filter_out(grid, sidecar, out)
+    _check(load_library().vbm_cross_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
+                                           int(sidecar.shape[1]), int(flags), _stream_ptr(stream)),
+           "vbm_cross_filter")
+    return out

@@ -1,0 +1,81 @@
+"""The host grid builder (vbm_build, in libvbm.so) against the oracle, byte for
+byte: leaf order, origins, value masks, prefix directories, leafFirst, block
+firstLeafID and jumpMap; plus the internal nodes' consistency.  No GPU."""
+import numpy as np
+import pytest
+
+import oracle
+from nanovdb_stencil_filtering_amd import inputs as I
+from nanovdb_stencil_filtering_amd import vbm
+
+GRIDS = {
+    "hand": lambda: np.array([[0, 0, 0], [0, 0, 1], [0, 1, 0], [1, 0, 0], [7, 7, 7], [8, 0, 0], [-1, 0, 0],
+                              [0, 0, 8], [128, 0, 0], [0, -1, 0], [0, 0, -8], [7, 0, 0]], np.int32),
+    "tiny_shell": lambda: I.shell_coords(**I.TINY_SHELL),
+    "straddle": lambda: I.random_sparse_coords(3, (18, 18, 18), 0.9, (4087, -9, -4100)),
+    "sparse_neg": lambda: I.random_sparse_coords(2, (40, 26, 22), 0.1, (-300, -5, 117)),
+    "one_per_leaf": lambda: I.one_per_cell_coords(5, 12),
+    "stress_small": lambda: I.leaf_bernoulli_coords(4, 2000, 20, (0.02, 0.1, 0.5, 1.0)),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(GRIDS))
+def pair(request):
+    coords = GRIDS[request.param]()
+    dup = np.concatenate([I.shuffled(coords, 1), coords[: len(coords) // 3]])
+    return oracle.OracleGrid(coords), dup
+
+
+@pytest.mark.parametrize("log2w", [6, 7, 8, 9])
+def test_builder_matches_oracle(pair, log2w):
+    ref, coords = pair
+    hdr, blob = vbm.build_host(coords, log2w)
+    assert hdr.magic == vbm.GRID_MAGIC and hdr.log2_width == log2w
+    assert hdr.n_active == ref.n_active and hdr.n_leaves == ref.n_leaves
+    assert hdr.n_blocks == ref.n_blocks(log2w)
+    s = vbm.blob_sections(hdr, blob)
+    lv = ref.leaves()
+    assert np.array_equal(s["leaves"]["origin"], lv["origin"])
+    assert np.array_equal(s["leaves"]["mask"], lv["mask"])
+    assert np.array_equal(s["leaves"]["prefix"], lv["prefix"])
+    assert np.array_equal(s["leaves"]["first"], lv["first"])
+    assert np.all(s["leaves"]["pad"] == 0)
+    b = ref.blocks(log2w)
+    assert np.array_equal(s["block_first_leaf"], b["first_leaf"])
+    assert np.array_equal(s["block_jump"], b["jump"])
+    for off in (hdr.off_leaves, hdr.off_root, hdr.off_upper, hdr.off_lower, hdr.off_block_first_leaf,
+                hdr.off_block_jump):
+        assert off % 256 == 0
+
+
+def test_tree_nodes_reach_every_leaf(pair):
+    ref, coords = pair
+    hdr, blob = vbm.build_host(coords, 7)
+    s = vbm.blob_sections(hdr, blob)
+    keys = s["root"]["key"].astype(np.int64)
+    order = np.lexsort((keys[:, 2], keys[:, 1], keys[:, 0]))
+    assert np.array_equal(order, np.arange(hdr.n_root))  # sorted, lexicographic
+    assert len({tuple(k) for k in keys.tolist()}) == hdr.n_root
+    o = s["leaves"]["origin"].astype(np.int64)
+    root_of = {tuple(k): int(u) for k, u in zip(keys.tolist(), s["root"]["upper"])}
+    for l in range(hdr.n_leaves):
+        x, y, z = o[l]
+        up = root_of[(x >> 12, y >> 12, z >> 12)]
+        lower = s["upper"][up, ((x >> 7) & 31) << 10 | ((y >> 7) & 31) << 5 | ((z >> 7) & 31)]
+        assert lower != 0xFFFFFFFF
+        assert s["lower"][lower, ((x >> 3) & 15) << 8 | ((y >> 3) & 15) << 4 | ((z >> 3) & 15)] == l
+    # every non-empty lower slot is a leaf, every non-empty upper slot a lower node
+    assert int((s["lower"] != 0xFFFFFFFF).sum()) == hdr.n_leaves
+    assert int((s["upper"] != 0xFFFFFFFF).sum()) == hdr.n_lower
+
+
+def test_empty_grid():
+    hdr, blob = vbm.build_host(np.zeros((0, 3), np.int32), 7)
+    assert hdr.n_active == 0 and hdr.n_blocks == 0 and hdr.n_leaves == 0
+
+
+def test_build_is_order_and_duplicate_invariant():
+    c = I.shell_coords(**I.TINY_SHELL)
+    h1, b1 = vbm.build_host(c, 8)
+    h2, b2 = vbm.build_host(np.concatenate([I.shuffled(c, 3), c[::7]]), 8)
+    assert bytes(h1) == bytes(h2) and np.array_equal(b1, b2)
