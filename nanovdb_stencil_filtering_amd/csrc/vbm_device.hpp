@@ -94,18 +94,31 @@ __device__ __forceinline__ uint32_t select_in_word(uint64_t m, uint32_t n) {
   return pos;
 }
 
-// 9-bit field k of the prefix directory: active voxels in mask words 0..k.
+// 9-bit field k (0..6) of the prefix directory: active voxels in mask words
+// 0..k.  Field k occupies bits 9k..9k+8 of the 64-bit directory; read with
+// 32-bit operations (funnel shift across the two halves).
 __device__ __forceinline__ uint32_t prefix_field(uint64_t dir, uint32_t k) {
-  return uint32_t(dir >> (9 * k)) & 511u;
+  const uint32_t lo = uint32_t(dir), hi = uint32_t(dir >> 32);
+  const uint32_t p = 9 * k;
+  const uint32_t x = p < 32 ? __builtin_amdgcn_alignbit(hi, lo, p) : (hi >> (p - 32));
+  return x & 511u;
 }
 
-// Index of voxel offset o in leaf L, 0 if the voxel is inactive.
+// Index of voxel offset o in leaf L, 0 if the voxel is inactive:
+// leafFirst + (active voxels in the words before o's word) + (active voxels
+// below o in its word).  32-bit operations on the two halves of the word.
 __device__ __forceinline__ uint32_t index_in_leaf(const Leaf& L, uint32_t o) {
   const uint32_t w = o >> 6, b = o & 63;
   const uint64_t m = L.mask[w];
+  const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+  const bool upper = b >= 32;
+  const uint32_t half = upper ? hi : lo;
+  const uint32_t sh = b & 31;
+  const uint32_t below = __builtin_amdgcn_ubfe(half, 0, sh);          // bits of the half below o
+  const uint32_t rank = __popc(below) + (upper ? __popc(lo) : 0u);
   const uint32_t before = w ? prefix_field(L.prefix, w - 1) : 0u;
-  const uint32_t idx = uint32_t(L.first) + before + uint32_t(__popcll(m & ((uint64_t(1) << b) - 1)));
-  return ((m >> b) & 1) ? idx : 0u;
+  const uint32_t idx = uint32_t(L.first) + before + rank;
+  return ((half >> sh) & 1u) ? idx : 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -121,20 +134,10 @@ __device__ __forceinline__ uint32_t block_span(const DeviceGrid& g, uint32_t b) 
   return span;
 }
 
-// Inverse-map decode of slot s of block b: the leaf is firstLeafID plus the
-// leaf starts at or before s; the rank of the slot inside its leaf picks the
-// mask word through the prefix directory, then an in-word select gives the
-// voxel offset.  O(1) per slot, no shared memory, divergence-safe.
-__device__ __forceinline__ Slot decode_slot(const DeviceGrid& g, uint32_t b, uint32_t s) {
-  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + s;
-  if (idx > g.n_active) return Slot{kSentinelLeaf, kSentinelOffset};
-  const uint32_t words = 1u << (g.log2w - 6);
-  const uint64_t* jm = g.block_jump + uint64_t(b) * words;
-  const uint32_t wi = s >> 6;
-  uint32_t rank = 0;
-  for (uint32_t k = 0; k < wi; ++k) rank += __popcll(jm[k]);
-  rank += __popcll(jm[wi] & ((uint64_t(2) << (s & 63)) - 1));  // bits 0..s
-  const uint32_t leaf = g.block_first_leaf[b] + rank;
+// Select stage of the decode: given the slot's leaf, the voxel's rank inside
+// the leaf picks the mask word through the prefix directory (the number of
+// fields <= rank), then an in-word select gives the voxel offset.
+__device__ __forceinline__ Slot select_in_leaf(const DeviceGrid& g, uint32_t leaf, uint64_t idx) {
   const Leaf& L = g.leaves[leaf];
   const uint32_t r = uint32_t(idx - L.first);  // rank of the voxel inside its leaf
   const uint64_t dir = L.prefix;
@@ -143,6 +146,51 @@ __device__ __forceinline__ Slot decode_slot(const DeviceGrid& g, uint32_t b, uin
   for (uint32_t k = 0; k < 7; ++k) word += prefix_field(dir, k) <= r ? 1u : 0u;
   const uint32_t before = word ? prefix_field(dir, word - 1) : 0u;
   return Slot{leaf, 64 * word + select_in_word(L.mask[word], r - before)};
+}
+
+// Set bits of the 64-bit word {hi, lo} at positions 0..b (inclusive).
+__device__ __forceinline__ uint32_t rank_inclusive(uint32_t lo, uint32_t hi, uint32_t b) {
+  const uint32_t sh = b & 31;
+  const uint32_t keep = (2u << sh) - 1u;  // bits 0..sh (all 32 when sh == 31)
+  return b < 32 ? __popc(lo & keep) : __popc(lo) + __popc(hi & keep);
+}
+
+// Inverse-map decode of slot s of block b: the leaf is firstLeafID plus the
+// leaf starts (jumpMap bits) at or before s, then select_in_leaf.  O(1) per
+// slot, no shared memory, divergence-safe; any slot may be passed.
+__device__ __forceinline__ Slot decode_slot(const DeviceGrid& g, uint32_t b, uint32_t s) {
+  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + s;
+  if (idx > g.n_active) return Slot{kSentinelLeaf, kSentinelOffset};
+  const uint32_t words = 1u << (g.log2w - 6);
+  const uint64_t* jm = g.block_jump + uint64_t(b) * words;
+  const uint32_t wi = s >> 6;
+  uint32_t rank = 0;
+  for (uint32_t k = 0; k < wi; ++k) rank += __popcll(jm[k]);
+  const uint64_t w = jm[wi];
+  rank += rank_inclusive(uint32_t(w), uint32_t(w >> 32), s & 63);
+  return select_in_leaf(g, g.block_first_leaf[b] + rank, idx);
+}
+
+// decode_slot for the calling work-item's own slot s = threadIdx.x of a
+// workgroup of W work-items (one wave64 per 64 slots).  The jumpMap word of
+// the wave is uniform, so the rank is a scalar popcount over the earlier
+// words plus the lane's rank in its wave's word (v_mbcnt over the two halves)
+// plus the lane's own bit.
+__device__ __forceinline__ Slot decode_own_slot(const DeviceGrid& g, uint32_t b) {
+  const uint32_t s = threadIdx.x;
+  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + s;
+  const uint32_t words = 1u << (g.log2w - 6);
+  const uint64_t* jm = g.block_jump + uint64_t(b) * words;
+  const uint32_t wi = __builtin_amdgcn_readfirstlane(s >> 6);  // wave index in the workgroup
+  uint32_t rank = 0;
+  for (uint32_t k = 0; k < wi; ++k) rank += __popcll(jm[k]);
+  const uint64_t w = jm[wi];
+  const uint32_t lo = uint32_t(w), hi = uint32_t(w >> 32);
+  const uint32_t lane = s & 63;
+  rank += __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));  // bits below the lane
+  rank += ((lane < 32 ? lo : hi) >> (lane & 31)) & 1u;                     // the lane's own bit
+  if (idx > g.n_active) return Slot{kSentinelLeaf, kSentinelOffset};
+  return select_in_leaf(g, g.block_first_leaf[b] + rank, idx);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,8 +267,11 @@ __device__ __forceinline__ void stage_neighbour_table(const DeviceGrid& g, uint3
     if (DIRS == 27) {
       dx = int(dir) / 9 - 1; dy = (int(dir) / 3) % 3 - 1; dz = int(dir) % 3 - 1;
     } else {
-      const int t = cross_box_tap(int(dir));
-      dx = box_di(t); dy = box_dj(t); dz = box_dk(t);
+      // cross order -x, -y, -z, centre, +z, +y, +x
+      const int d = int(dir);
+      const int axis = d < 3 ? d : 6 - d;  // 0 = x, 1 = y, 2 = z (3 = centre)
+      const int sign = d < 3 ? -1 : (d > 3 ? 1 : 0);
+      dx = axis == 0 ? sign : 0; dy = axis == 1 ? sign : 0; dz = axis == 2 ? sign : 0;
     }
     const Leaf& L = g.leaves[first_leaf + j];
     table[e] = (dx | dy | dz) ? find_leaf(g, L.origin[0] + 8 * dx, L.origin[1] + 8 * dy, L.origin[2] + 8 * dz)

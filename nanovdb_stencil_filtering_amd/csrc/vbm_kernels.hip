@@ -78,7 +78,7 @@ __device__ __forceinline__ const float* tap_row(const float* __restrict__ sc, ui
 
 __global__ void __launch_bounds__(512) k_decode(DeviceGrid g, uint32_t* __restrict__ leaf_index,
                                                 uint16_t* __restrict__ voxel_offset) {
-  const Slot s = decode_slot(g, blockIdx.x, threadIdx.x);
+  const Slot s = decode_own_slot(g, blockIdx.x);
   const uint64_t row = (uint64_t(blockIdx.x) << g.log2w) + threadIdx.x;
   leaf_index[row] = s.leaf;
   voxel_offset[row] = uint16_t(s.offset);
@@ -89,7 +89,7 @@ template <int SHAPE, bool CACHED, bool STREAM>
 __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict__ taps) {
   __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * SHAPE : 1];
   const uint32_t b = blockIdx.x;
-  const Slot s = decode_slot(g, b, threadIdx.x);
+  const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
   uint64_t* out = taps + ((uint64_t(b) << g.log2w) + threadIdx.x) * SHAPE;
   bool cached = false;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(512) k_box(DeviceGrid g, const float* __restri
   __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * kBoxTaps : 1];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
-  const Slot s = decode_slot(g, b, threadIdx.x);
+  const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
   bool cached = false;
   uint32_t first = 0;
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __rest
   __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * kCrossTaps : 1];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
-  const Slot s = decode_slot(g, b, threadIdx.x);
+  const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
   bool cached = false;
   uint32_t first = 0;
