@@ -76,18 +76,26 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="profile mode: run only this variant (e.g. box_cs) and exit")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="profile mode: time a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the VBM pipeline here is a single-GPU build "
               "(see the sharding note in DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from nanovdb_stencil_filtering_amd import inputs, vbm
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy:
+        n = args.calib_copy << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = time_launches(lambda k: dst.copy_(src), 1, args.steps, args.warmup)
+        log("calib-copy %d MiB: %.4f ms/copy, %.1f GB/s (read+write)" % (args.calib_copy, ms, 2 * n * 4 / ms / 1e6))
+        return
     vbm.load_library()
     C = args.channels
     log("bench: generating cfg-shell")

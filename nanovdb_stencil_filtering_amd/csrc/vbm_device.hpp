@@ -296,6 +296,98 @@ __device__ __forceinline__ uint32_t resolve_cached(const DeviceGrid& g, const ui
 }
 
 // ---------------------------------------------------------------------------
+// cached resolution, brick form: per spanned leaf, a dense 10^3 block of
+// resolved taps in LDS
+// ---------------------------------------------------------------------------
+//
+// After the neighbour-leaf table is staged, the workgroup resolves once, for
+// each spanned leaf, every position of the leaf grown by one voxel on each side
+// (10 x 10 x 10 positions, the union of the 27-tap stencils of its voxels).
+// Entry (x+1, y+1, z+1) holds the resolved tap of local position (x, y, z),
+// x, y, z in -1..8, encoded as value = index * scale, or `sentinel` when
+// inactive.  A voxel at (x, y, z) then finds tap (di, dj, dk) at entry
+// (x+1+di, y+1+dj, z+1+dk): 27 LDS reads at fixed offsets from one address.
+// Positions are resolved one (x, y) column at a time: the column's mask byte
+// and the index of its first voxel come from one mask word of the centre
+// leaf (z 0..7) and of its -z / +z neighbours (z = -1, z = 8).
+constexpr int kBrickEdge = 10;
+constexpr int kBrickCells = kBrickEdge * kBrickEdge * kBrickEdge;
+
+struct ColumnBits {
+  uint32_t bits;  // active voxels of the column at z = 0..7 (bit z)
+  uint32_t base;  // index of the column's first active voxel, if any
+};
+
+// Column (wx, y) of leaf `leaf`: mask byte ((y & 7) of word wx) and the index
+// of its first voxel.  kNoLeaf gives an empty column.
+__device__ __forceinline__ ColumnBits column_bits(const DeviceGrid& g, uint32_t leaf, uint32_t wx, uint32_t y8) {
+  const bool ok = leaf != kNoLeaf;
+  const Leaf& L = g.leaves[ok ? leaf : 0u];
+  const uint64_t m = L.mask[wx];
+  const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+  const bool upper = y8 >= 32;
+  const uint32_t half = upper ? hi : lo;
+  const uint32_t sh = y8 & 31;
+  const uint32_t below = __popc(__builtin_amdgcn_ubfe(half, 0, sh)) + (upper ? __popc(lo) : 0u);
+  const uint32_t before = wx ? prefix_field(L.prefix, wx - 1) : 0u;
+  const uint32_t bits = __builtin_amdgcn_ubfe(half, sh, 8);
+  return ColumnBits{ok ? bits : 0u, uint32_t(L.first) + before + below};
+}
+
+// Resolve the bricks of `count` spanned leaves whose neighbour tables are
+// table[jj * 27 + dir], jj < count, into brick[jj * kBrickCells + ...].  All
+// threads of the block; ends with a barrier.
+__device__ __forceinline__ void build_bricks(const DeviceGrid& g, const uint32_t* table, uint32_t count,
+                                             uint32_t scale, uint32_t sentinel, uint32_t* brick) {
+  for (uint32_t c = threadIdx.x; c < count * 100; c += blockDim.x) {
+    const uint32_t jj = c / 100, xy = c - jj * 100;
+    const uint32_t xp = xy / 10, yp = xy - xp * 10;
+    const int x = int(xp) - 1, y = int(yp) - 1;
+    const int dxl = x >> 3, dyl = y >> 3;  // -1, 0, +1
+    const uint32_t wx = uint32_t(x) & 7, y8 = (uint32_t(y) & 7) << 3;
+    const uint32_t* trow = table + jj * 27 + (dxl + 1) * 9 + (dyl + 1) * 3;
+    const ColumnBits zm = column_bits(g, trow[0], wx, y8);  // -z neighbour, its z = 7
+    const ColumnBits zc = column_bits(g, trow[1], wx, y8);  // the leaf column, z = 0..7
+    const ColumnBits zp = column_bits(g, trow[2], wx, y8);  // +z neighbour, its z = 0
+    uint32_t* out = brick + jj * kBrickCells + xp * 100 + yp * 10;
+    out[0] = ((zm.bits >> 7) & 1u) ? (zm.base + __popc(zm.bits & 0x7Fu)) * scale : sentinel;
+#pragma unroll
+    for (uint32_t z = 0; z < 8; ++z)
+      out[1 + z] = ((zc.bits >> z) & 1u) ? (zc.base + __popc(zc.bits & ((1u << z) - 1u))) * scale : sentinel;
+    out[9] = (zp.bits & 1u) ? zp.base * scale : sentinel;
+  }
+  __syncthreads();
+}
+
+// Stage the neighbour-leaf table of the `count` spanned leaves starting at
+// leaf `first` (all threads; ends with a barrier).
+__device__ __forceinline__ void stage_table_range(const DeviceGrid& g, uint32_t first, uint32_t count,
+                                                  uint32_t* table) {
+  for (uint32_t e = threadIdx.x; e < count * 27; e += blockDim.x) {
+    const uint32_t j = e / 27, dir = e - j * 27;
+    const int dx = int(dir) / 9 - 1, dy = (int(dir) / 3) % 3 - 1, dz = int(dir) % 3 - 1;
+    const Leaf& L = g.leaves[first + j];
+    table[e] = (dx | dy | dz) ? find_leaf(g, L.origin[0] + 8 * dx, L.origin[1] + 8 * dy, L.origin[2] + 8 * dz)
+                              : first + j;
+  }
+  __syncthreads();
+}
+
+// Address of the (-1, -1, -1) tap of the voxel at local offset o in brick jj;
+// tap t of the box is at offset box_brick_offset(t) from it.
+__device__ __forceinline__ const uint32_t* brick_corner(const uint32_t* brick, uint32_t jj, uint32_t o) {
+  return brick + jj * kBrickCells + (o >> 6) * 100 + ((o >> 3) & 7) * 10 + (o & 7);
+}
+__host__ __device__ constexpr int box_brick_offset(int t) { return (t / 9) * 100 + ((t / 3) % 3) * 10 + t % 3; }
+
+// Brick-cached box: the 27 taps streamed to f(t, value) in tap order.
+template <class F>
+__device__ __forceinline__ void for_each_box_brick(const uint32_t* corner, F&& f) {
+#pragma unroll
+  for (int t = 0; t < kBoxTaps; ++t) f(t, corner[box_brick_offset(t)]);
+}
+
+// ---------------------------------------------------------------------------
 // resolvers: streamed (forEach) and materialised (compute) forms
 // ---------------------------------------------------------------------------
 

@@ -25,18 +25,44 @@ using namespace vbm;
 
 namespace {
 
-// Row of zeros read by inactive taps (up to 16 channels per launch chunk).
-__device__ __align__(64) float g_zero_row[16];
+// ---------------------------------------------------------------------------
+// sidecar access through a bounds-checked buffer resource
+// ---------------------------------------------------------------------------
+// Raw buffer loads whose offset is at or beyond num_records return zeros.  An
+// inactive tap carries the offset kInactive, so it adds +0 without a branch
+// or a pointer select.  Rows of the sidecar must therefore end below kInactive
+// bytes (checked on the host).
+constexpr uint32_t kInactive = 0xFFFFFF00u;
+constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3
 
-// ---------------------------------------------------------------------------
-// row I/O: CH channels starting at p; VEC = 16-byte aligned float4 access
-// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Sidecar {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_bytes;  // C * 4
+};
+
+__device__ __forceinline__ Sidecar make_sidecar(const float* sc, uint32_t bytes, uint32_t C, uint32_t ch0) {
+  Sidecar s;
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc + ch0), short(0), int(bytes - 4 * ch0),
+                                             int(kBufferFlags));
+  s.row_bytes = 4 * C;
+  return s;
+}
+
+__device__ __forceinline__ uint32_t tap_offset(const Sidecar& s, uint32_t idx) {
+  return idx ? idx * s.row_bytes : kInactive;
+}
+
+// acc[c] += row[c] for the CH channels at byte offset `off` (kInactive: zeros).
 template <int CH, bool VEC>
-__device__ __forceinline__ void add_row(float (&acc)[CH], const float* __restrict__ p) {
+__device__ __forceinline__ void add_row(float (&acc)[CH], const Sidecar& s, uint32_t off) {
   if constexpr (VEC && CH % 4 == 0) {
 #pragma unroll
     for (int q = 0; q < CH / 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(p)[q];
+      // whole-vector bit cast: indexing the u32 vector element by element made
+      // clang emit a single dword load for all four channels
+      const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off + 16 * q, 0, 0));
       acc[4 * q + 0] = acc[4 * q + 0] + v.x;
       acc[4 * q + 1] = acc[4 * q + 1] + v.y;
       acc[4 * q + 2] = acc[4 * q + 2] + v.z;
@@ -44,7 +70,63 @@ __device__ __forceinline__ void add_row(float (&acc)[CH], const float* __restric
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = acc[c] + p[c];
+    for (int c = 0; c < CH; ++c)
+      acc[c] = acc[c] + __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, off + 4 * c, 0, 0));
+  }
+}
+
+// The CH channels at byte offset `off`, loaded into registers (no use yet).
+template <int CH, bool VEC>
+struct Row {
+  static constexpr int kVec = (VEC && CH % 4 == 0) ? CH / 4 : 0;
+  f32x4 v[kVec ? kVec : 1];
+  float f[kVec ? 1 : CH];
+  __device__ __forceinline__ void load(const Sidecar& s, uint32_t off) {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int q = 0; q < kVec; ++q)
+        v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off + 16 * q, 0, 0));
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        f[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, off + 4 * c, 0, 0));
+    }
+  }
+  __device__ __forceinline__ void add_to(float (&acc)[CH]) const {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int q = 0; q < kVec; ++q) {
+        acc[4 * q + 0] = acc[4 * q + 0] + v[q].x;
+        acc[4 * q + 1] = acc[4 * q + 1] + v[q].y;
+        acc[4 * q + 2] = acc[4 * q + 2] + v[q].z;
+        acc[4 * q + 3] = acc[4 * q + 3] + v[q].w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[c] = acc[c] + f[c];
+    }
+  }
+};
+
+// Gather-accumulate of the 27 box taps in tap order, software pipelined:
+// the rows of taps t+1..t+D are in flight while tap t is added, and the
+// scheduler is fenced between steps so it cannot hoist all 27 rows at once
+// (which costs more registers than a wave can hold).  off(t) gives the byte
+// offset of tap t (kInactive for an inactive tap).
+template <int CH, bool VEC, int D, class Off>
+__device__ __forceinline__ void gather_box_pipelined(float (&acc)[CH], const Sidecar& s, Off&& off) {
+  Row<CH, VEC> buf[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) buf[t].load(s, off(t));
+#pragma unroll
+  for (int t = 0; t < kBoxTaps; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+    buf[t % D].add_to(acc);
+    // Keep tap t's adds here: without this the compiler sinks every add below
+    // the tree walks of later taps and keeps all 27 rows live.  Emits nothing.
+#pragma unroll
+    for (int c = 0; c < CH; ++c) asm volatile("" : "+v"(acc[c]));
+    if (t + D < kBoxTaps) buf[t % D].load(s, off(t + D));
   }
 }
 
@@ -68,9 +150,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
   }
 }
 
-__device__ __forceinline__ const float* tap_row(const float* __restrict__ sc, uint32_t idx, uint32_t C, uint32_t ch0) {
-  return idx ? sc + uint64_t(idx) * C + ch0 : g_zero_row;
-}
+// Dynamic LDS of the brick-cached kernels: the neighbour table of up to `cap`
+// spanned leaves, then their bricks.
+__host__ __device__ constexpr uint32_t brick_lds_bytes(uint32_t cap) { return cap * 27 * 4 + cap * kBrickCells * 4; }
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -84,7 +166,49 @@ __global__ void __launch_bounds__(512) k_decode(DeviceGrid g, uint32_t* __restri
   voxel_offset[row] = uint16_t(s.offset);
 }
 
-// Raw taps of every slot.  SHAPE 27 (box) or 7 (cross).
+// Raw box taps through the brick cache (materialised or streamed), block by
+// block in passes of at most `cap` spanned leaves; blocks spanning more than
+// kMaxCachedLeaves walk the tree per tap.
+template <bool STREAM>
+__global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t* __restrict__ taps, uint32_t cap) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* table = lds;
+  uint32_t* brick = lds + cap * 27;
+  const uint32_t b = blockIdx.x;
+  const Slot s = decode_own_slot(g, b);
+  const bool valid = s.leaf != kSentinelLeaf;
+  uint64_t* out = taps + ((uint64_t(b) << g.log2w) + threadIdx.x) * kBoxTaps;
+  const uint32_t first = g.block_first_leaf[b];
+  const uint32_t span = block_span(g, b);  // block-uniform: every barrier below is uniform
+  if (span > kMaxCachedLeaves) {
+    if (valid) for_each_box(g, s, [&](int t, uint32_t idx) { out[t] = idx; });
+  } else {
+    const uint32_t j = valid ? s.leaf - first : 0xFFFFFFFFu;
+    for (uint32_t j0 = 0; j0 < span; j0 += cap) {
+      const uint32_t count = min(cap, span - j0);
+      if (j0) __syncthreads();
+      stage_table_range(g, first + j0, count, table);
+      build_bricks(g, table, count, 1u, 0u, brick);
+      if (j - j0 < count) {
+        const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
+        if constexpr (STREAM) {
+          for_each_box_brick(corner, [&](int t, uint32_t idx) { out[t] = idx; });
+        } else {
+          uint32_t st[kBoxTaps];
+          for_each_box_brick(corner, [&](int t, uint32_t idx) { st[t] = idx; });
+#pragma unroll
+          for (int t = 0; t < kBoxTaps; ++t) out[t] = st[t];
+        }
+      }
+    }
+  }
+  if (!valid) {
+#pragma unroll
+    for (int t = 0; t < kBoxTaps; ++t) out[t] = 0;
+  }
+}
+
+// Raw taps by the tree walk (box or cross) and by the per-tap cached table (cross).
 template <int SHAPE, bool CACHED, bool STREAM>
 __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict__ taps) {
   __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * SHAPE : 1];
@@ -109,13 +233,10 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
   }
   if constexpr (SHAPE == 27) {
     if constexpr (STREAM) {
-      auto put = [&](int t, uint32_t idx) { out[t] = idx; };
-      if (cached) for_each_box_cached(g, table, first, s, put);
-      else for_each_box(g, s, put);
+      for_each_box(g, s, [&](int t, uint32_t idx) { out[t] = idx; });
     } else {
       uint64_t st[kBoxTaps];
-      if (cached) compute_box_cached(g, table, first, s, st);
-      else compute_box(g, s, st);
+      compute_box(g, s, st);
 #pragma unroll
       for (int t = 0; t < kBoxTaps; ++t) out[t] = st[t];
     }
@@ -128,48 +249,88 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
   }
 }
 
-// 27-tap box filter over channels [ch0, ch0 + CH) of a C-channel sidecar.
-template <int CH, bool VEC, bool CACHED, bool STREAM>
-__global__ void __launch_bounds__(512) k_box(DeviceGrid g, const float* __restrict__ sc, float* __restrict__ out,
-                                             uint32_t C, uint32_t ch0) {
-  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * kBoxTaps : 1];
+// 27-tap box filter, tree-walk resolution, over channels [ch0, ch0 + CH).
+template <int CH, bool VEC, bool STREAM>
+__global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                                   float* __restrict__ out, uint32_t C, uint32_t ch0) {
+  constexpr int kPipe = CH >= 8 ? 2 : 4;  // taps in flight per work-item
+  const uint32_t b = blockIdx.x;
+  zero_index_row<CH>(out, ch0);
+  const Slot s = decode_own_slot(g, b);
+  if (s.leaf == kSentinelLeaf) return;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  float acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+  if constexpr (STREAM) {
+    // each tap resolved by its tree walk as the gather pipeline asks for it
+    const VoxelCoord p = voxel_coord(g, s);
+    gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) {
+      return tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+    });
+  } else {
+    uint64_t st[kBoxTaps];
+    compute_box(g, s, st);
+    gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return tap_offset(side, uint32_t(st[t])); });
+  }
+  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
+  store_row<CH, VEC>(out + idx * C + ch0, acc);
+}
+
+// 27-tap box filter through the brick cache (materialised or streamed taps).
+template <int CH, bool VEC, bool STREAM>
+__global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                                    float* __restrict__ out, uint32_t C, uint32_t ch0, uint32_t cap) {
+  constexpr int kPipe = CH >= 8 ? 2 : 4;  // taps in flight per work-item
+  extern __shared__ uint32_t lds[];
+  uint32_t* table = lds;
+  uint32_t* brick = lds + cap * 27;
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
-  bool cached = false;
-  uint32_t first = 0;
-  if constexpr (CACHED) {
-    first = g.block_first_leaf[b];
-    const uint32_t span = block_span(g, b);
-    if (span <= kMaxCachedLeaves) {
-      stage_neighbour_table<kBoxTaps>(g, first, span, table);
-      cached = true;
-    }
-  }
-  if (!valid) return;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
   float acc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
-  auto gather = [&](int, uint32_t idx) { add_row<CH, VEC>(acc, tap_row(sc, idx, C, ch0)); };
-  if constexpr (STREAM) {
-    if (cached) for_each_box_cached(g, table, first, s, gather);
-    else for_each_box(g, s, gather);
+  const uint32_t first = g.block_first_leaf[b];
+  const uint32_t span = block_span(g, b);  // block-uniform: every barrier below is uniform
+  if (span > kMaxCachedLeaves) {
+    if (valid) {  // per-tap tree walk
+      const VoxelCoord p = voxel_coord(g, s);
+      gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) {
+        return tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+      });
+    }
   } else {
-    uint64_t st[kBoxTaps];
-    if (cached) compute_box_cached(g, table, first, s, st);
-    else compute_box(g, s, st);
-#pragma unroll
-    for (int t = 0; t < kBoxTaps; ++t) gather(t, uint32_t(st[t]));
+    const uint32_t j = valid ? s.leaf - first : 0xFFFFFFFFu;
+    for (uint32_t j0 = 0; j0 < span; j0 += cap) {
+      const uint32_t count = min(cap, span - j0);
+      if (j0) __syncthreads();
+      stage_table_range(g, first + j0, count, table);
+      build_bricks(g, table, count, side.row_bytes, kInactive, brick);
+      if (j - j0 < count) {
+        const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
+        if constexpr (STREAM) {
+          // taps streamed from the brick as the pipeline consumes them
+          gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return corner[box_brick_offset(t)]; });
+        } else {
+          uint32_t st[kBoxTaps];
+          for_each_box_brick(corner, [&](int t, uint32_t off) { st[t] = off; });
+          gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return st[t]; });
+        }
+      }
+    }
   }
+  if (!valid) return;
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   store_row<CH, VEC>(out + idx * C + ch0, acc);
 }
 
 // 7-tap cross filter: sum, or 7-point Laplacian (faces in cross order) - fl(6 c).
 template <int CH, bool VEC, bool CACHED, bool LAP>
-__global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __restrict__ sc, float* __restrict__ out,
-                                               uint32_t C, uint32_t ch0) {
+__global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                               float* __restrict__ out, uint32_t C, uint32_t ch0) {
   __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * kCrossTaps : 1];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
@@ -186,6 +347,7 @@ __global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __rest
     }
   }
   if (!valid) return;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
   uint64_t st[kCrossTaps];
   if (cached) compute_cross_cached(g, table, first, s, st);
   else compute_cross(g, s, st);
@@ -195,14 +357,14 @@ __global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __rest
 #pragma unroll
   for (int j = 0; j < kCrossTaps; ++j) {
     if (LAP && j == 3) continue;  // the centre enters the Laplacian only as -6*centre
-    add_row<CH, VEC>(acc, tap_row(sc, uint32_t(st[j]), C, ch0));
+    add_row<CH, VEC>(acc, side, tap_offset(side, uint32_t(st[j])));
   }
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   if constexpr (LAP) {
     float centre[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) centre[c] = 0.0f;
-    add_row<CH, VEC>(centre, sc + idx * C + ch0);
+    add_row<CH, VEC>(centre, side, uint32_t(idx) * side.row_bytes);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const float six_c = 6.0f * centre[c];
@@ -260,6 +422,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? VBM_OK : VBM_ERR_
 
 int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out, int C) {
   if (!sc || !out || C < 1) return VBM_ERR_ARG;
+  if ((grid->n_active + 1) * uint64_t(C) * 4 > kInactive) return VBM_ERR_SIZE;
   if ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 3) return VBM_ERR_ALIGN;
   const uint64_t bytes = (grid->n_active + 1) * uint64_t(C) * 4;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(sc), b0 = reinterpret_cast<uintptr_t>(out);
@@ -267,21 +430,33 @@ int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out,
   return VBM_OK;
 }
 
+// Brick capacity (spanned leaves resolved per pass) for BlockWidth 2^log2w:
+// one pass covers about 98% of the blocks of a sphere shell.
+uint32_t brick_capacity(int log2w) { return log2w <= 6 ? 3u : log2w == 7 ? 4u : log2w == 8 ? 6u : 8u; }
+
 template <bool CACHED, bool STREAM>
 struct BoxLauncher {
   template <int CH, bool VEC>
-  static void go(const DeviceGrid& g, const float* sc, float* out, uint32_t C, uint32_t ch0, hipStream_t st) {
-    hipLaunchKernelGGL((k_box<CH, VEC, CACHED, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc, out,
-                       C, ch0);
+  static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
+                 hipStream_t st) {
+    if constexpr (CACHED) {
+      const uint32_t cap = brick_capacity(g.log2w);
+      hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w),
+                         brick_lds_bytes(cap), st, g, sc, bytes, out, C, ch0, cap);
+    } else {
+      hipLaunchKernelGGL((k_box_plain<CH, VEC, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc,
+                         bytes, out, C, ch0);
+    }
   }
 };
 
 template <bool CACHED, bool LAP>
 struct CrossLauncher {
   template <int CH, bool VEC>
-  static void go(const DeviceGrid& g, const float* sc, float* out, uint32_t C, uint32_t ch0, hipStream_t st) {
-    hipLaunchKernelGGL((k_cross<CH, VEC, CACHED, LAP>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc, out,
-                       C, ch0);
+  static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
+                 hipStream_t st) {
+    hipLaunchKernelGGL((k_cross<CH, VEC, CACHED, LAP>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc,
+                       bytes, out, C, ch0);
   }
 };
 
@@ -290,34 +465,35 @@ struct CrossLauncher {
 // multiple of 4 and both buffers are 16-byte aligned.
 template <class L>
 void launch_channels(const DeviceGrid& g, const float* sc, float* out, int C, hipStream_t st) {
+  const uint32_t bytes = uint32_t((uint64_t(g.n_active) + 1) * uint64_t(C) * 4);
   const bool vec = ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 15) == 0 && C % 4 == 0;
   const uint32_t uc = uint32_t(C);
   switch (C) {
-    case 1: L::template go<1, false>(g, sc, out, uc, 0, st); return;
-    case 2: L::template go<2, false>(g, sc, out, uc, 0, st); return;
-    case 3: L::template go<3, false>(g, sc, out, uc, 0, st); return;
+    case 1: L::template go<1, false>(g, sc, bytes, out, uc, 0, st); return;
+    case 2: L::template go<2, false>(g, sc, bytes, out, uc, 0, st); return;
+    case 3: L::template go<3, false>(g, sc, bytes, out, uc, 0, st); return;
     default: break;
   }
   uint32_t ch0 = 0;
   while (ch0 < uc) {
     const uint32_t left = uc - ch0;
     if (left >= 16) {
-      if (vec) L::template go<16, true>(g, sc, out, uc, ch0, st);
-      else L::template go<16, false>(g, sc, out, uc, ch0, st);
+      if (vec) L::template go<16, true>(g, sc, bytes, out, uc, ch0, st);
+      else L::template go<16, false>(g, sc, bytes, out, uc, ch0, st);
       ch0 += 16;
     } else if (left >= 8) {
-      if (vec) L::template go<8, true>(g, sc, out, uc, ch0, st);
-      else L::template go<8, false>(g, sc, out, uc, ch0, st);
+      if (vec) L::template go<8, true>(g, sc, bytes, out, uc, ch0, st);
+      else L::template go<8, false>(g, sc, bytes, out, uc, ch0, st);
       ch0 += 8;
     } else if (left >= 4) {
-      if (vec) L::template go<4, true>(g, sc, out, uc, ch0, st);
-      else L::template go<4, false>(g, sc, out, uc, ch0, st);
+      if (vec) L::template go<4, true>(g, sc, bytes, out, uc, ch0, st);
+      else L::template go<4, false>(g, sc, bytes, out, uc, ch0, st);
       ch0 += 4;
     } else if (left >= 2) {
-      L::template go<2, false>(g, sc, out, uc, ch0, st);
+      L::template go<2, false>(g, sc, bytes, out, uc, ch0, st);
       ch0 += 2;
     } else {
-      L::template go<1, false>(g, sc, out, uc, ch0, st);
+      L::template go<1, false>(g, sc, bytes, out, uc, ch0, st);
       ch0 += 1;
     }
   }
@@ -351,8 +527,11 @@ extern "C" int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool cached = flags & VBM_CACHED, stream_taps = flags & VBM_STREAMING;
   if (shape == 27) {
-    if (cached && stream_taps) hipLaunchKernelGGL((k_taps<27, true, true>), gd, bd, 0, st, g, d_taps);
-    else if (cached) hipLaunchKernelGGL((k_taps<27, true, false>), gd, bd, 0, st, g, d_taps);
+    const uint32_t cap = brick_capacity(g.log2w);
+    if (cached && stream_taps)
+      hipLaunchKernelGGL((k_taps_box_cached<true>), gd, bd, brick_lds_bytes(cap), st, g, d_taps, cap);
+    else if (cached)
+      hipLaunchKernelGGL((k_taps_box_cached<false>), gd, bd, brick_lds_bytes(cap), st, g, d_taps, cap);
     else if (stream_taps) hipLaunchKernelGGL((k_taps<27, false, true>), gd, bd, 0, st, g, d_taps);
     else hipLaunchKernelGGL((k_taps<27, false, false>), gd, bd, 0, st, g, d_taps);
   } else {

@@ -45,3 +45,13 @@ def test_kernels_present(device_asm):
     names = [n for n, _ in kernels(device_asm)]
     for k in ("k_decode", "k_taps", "k_box", "k_cross"):
         assert any(k in n for n in names), k
+
+
+def test_vector_sidecar_loads_are_16_bytes(device_asm):
+    """The float4 path must load 16 bytes per instruction (an element-wise
+    extraction of the buffer-load vector once collapsed into one dword load
+    reused for all four channels)."""
+    for name, body in kernels(device_asm):
+        if "k_box" in name and "ILi16ELb1E" in name:
+            assert "buffer_load_dwordx4" in body, name
+            assert "buffer_load_dword " not in body.replace("buffer_load_dwordx4", ""), name
