@@ -74,7 +74,9 @@ typedef enum vbm_status {
  *                                     active voxels in mask words 0..k
  *                       u64 first     index of the leaf's first active voxel
  *                       i32 origin[3] leaf min corner
- *                       36 bytes of zero padding
+ *                       u32 lower     parent lower node
+ *                       u32 upper     parent upper node (its root tile)
+ *                       28 bytes of zero padding
  *   root              n_root tiles of 16 bytes: i32 key[3] (= origin >> 12), u32 upper node;
  *                     sorted by key, lexicographic, signed
  *   upper             n_upper nodes of 32768 u32: lower-node id or 0xFFFFFFFF, slot

@@ -67,7 +67,9 @@ struct LeafRecord {
   uint64_t prefix;
   uint64_t first;
   int32_t origin[3];
-  uint32_t pad[9];
+  uint32_t lower;  // parent lower node
+  uint32_t upper;  // parent upper node (= root tile)
+  uint32_t pad[7];
 };
 static_assert(sizeof(LeafRecord) == 128, "leaf record is one 128-byte line");
 
@@ -156,6 +158,8 @@ extern "C" int vbm_build(const int32_t* ijk, int64_t n, int log2_width, vbm_grid
         lower.resize(lower.size() + 4096, kNone);
       }
       lower[lower.size() - 4096 + (leaf_key[l] & 4095)] = uint32_t(l);
+      leaves[l].lower = uint32_t(lower.size() / 4096 - 1);
+      leaves[l].upper = uint32_t(lower_key >> 15);
     }
     const uint64_t n_lower = lower.size() / 4096;
 

@@ -38,7 +38,9 @@ struct alignas(16) Leaf {  // 128 bytes: one cache line
   uint64_t prefix;
   uint64_t first;
   int32_t origin[3];
-  uint32_t pad[9];
+  uint32_t lower;  // parent lower node
+  uint32_t upper;  // parent upper node
+  uint32_t pad[7];
 };
 static_assert(sizeof(Leaf) == 128, "leaf record");
 
@@ -225,6 +227,24 @@ __device__ __forceinline__ uint32_t resolve_tree(const DeviceGrid& g, int32_t x,
   return index_in_leaf(g.leaves[leaf], (uint32_t(x) & 7) << 6 | (uint32_t(y) & 7) << 3 | (uint32_t(z) & 7));
 }
 
+// Leaf at offset (8 dx, 8 dy, 8 dz) from leaf L (kNoLeaf if none), found
+// from L's parents: inside L's lower node it is one lower-node entry; inside
+// its upper node, an upper-node entry then a lower-node entry; otherwise a
+// root-down walk.  Same answer as find_leaf at the neighbour's origin.
+__device__ __forceinline__ uint32_t neighbour_leaf(const DeviceGrid& g, const Leaf& L, int dx, int dy, int dz) {
+  const int32_t ox = L.origin[0], oy = L.origin[1], oz = L.origin[2];
+  const int32_t x = ox + 8 * dx, y = oy + 8 * dy, z = oz + 8 * dz;
+  const uint32_t lslot = ((uint32_t(x) >> 3) & 15) << 8 | ((uint32_t(y) >> 3) & 15) << 4 | ((uint32_t(z) >> 3) & 15);
+  if (((x ^ ox) | (y ^ oy) | (z ^ oz)) >> 7 == 0) return g.lower[uint64_t(L.lower) * 4096 + lslot];
+  if (((x ^ ox) | (y ^ oy) | (z ^ oz)) >> 12 == 0) {
+    const uint32_t uslot =
+        ((uint32_t(x) >> 7) & 31) << 10 | ((uint32_t(y) >> 7) & 31) << 5 | ((uint32_t(z) >> 7) & 31);
+    const uint32_t lower = g.upper[uint64_t(L.upper) * 32768 + uslot];
+    return lower == kNoLeaf ? kNoLeaf : g.lower[uint64_t(lower) * 4096 + lslot];
+  }
+  return find_leaf(g, x, y, z);
+}
+
 // ---------------------------------------------------------------------------
 // stencil shapes
 // ---------------------------------------------------------------------------
@@ -273,9 +293,7 @@ __device__ __forceinline__ void stage_neighbour_table(const DeviceGrid& g, uint3
       const int sign = d < 3 ? -1 : (d > 3 ? 1 : 0);
       dx = axis == 0 ? sign : 0; dy = axis == 1 ? sign : 0; dz = axis == 2 ? sign : 0;
     }
-    const Leaf& L = g.leaves[first_leaf + j];
-    table[e] = (dx | dy | dz) ? find_leaf(g, L.origin[0] + 8 * dx, L.origin[1] + 8 * dy, L.origin[2] + 8 * dz)
-                              : first_leaf + j;
+    table[e] = (dx | dy | dz) ? neighbour_leaf(g, g.leaves[first_leaf + j], dx, dy, dz) : first_leaf + j;
   }
   __syncthreads();
 }
@@ -359,17 +377,22 @@ __device__ __forceinline__ void build_bricks(const DeviceGrid& g, const uint32_t
   __syncthreads();
 }
 
+// Fill the neighbour-leaf table of the `count` spanned leaves starting at
+// leaf `first`, entries e = worker, worker + workers, ... (no barrier).
+__device__ __forceinline__ void fill_table_range(const DeviceGrid& g, uint32_t first, uint32_t count,
+                                                 uint32_t* table, uint32_t worker, uint32_t workers) {
+  for (uint32_t e = worker; e < count * 27; e += workers) {
+    const uint32_t j = e / 27, dir = e - j * 27;
+    const int dx = int(dir) / 9 - 1, dy = (int(dir) / 3) % 3 - 1, dz = int(dir) % 3 - 1;
+    table[e] = (dx | dy | dz) ? neighbour_leaf(g, g.leaves[first + j], dx, dy, dz) : first + j;
+  }
+}
+
 // Stage the neighbour-leaf table of the `count` spanned leaves starting at
 // leaf `first` (all threads; ends with a barrier).
 __device__ __forceinline__ void stage_table_range(const DeviceGrid& g, uint32_t first, uint32_t count,
                                                   uint32_t* table) {
-  for (uint32_t e = threadIdx.x; e < count * 27; e += blockDim.x) {
-    const uint32_t j = e / 27, dir = e - j * 27;
-    const int dx = int(dir) / 9 - 1, dy = (int(dir) / 3) % 3 - 1, dz = int(dir) % 3 - 1;
-    const Leaf& L = g.leaves[first + j];
-    table[e] = (dx | dy | dz) ? find_leaf(g, L.origin[0] + 8 * dx, L.origin[1] + 8 * dy, L.origin[2] + 8 * dz)
-                              : first + j;
-  }
+  fill_table_range(g, first, count, table, threadIdx.x, blockDim.x);
   __syncthreads();
 }
 

@@ -150,6 +150,43 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
   }
 }
 
+// Tunables of the brick-cached box kernel (defaults measured on MI355X).
+#ifndef VBM_PIPE_WIDE
+#define VBM_PIPE_WIDE 2   // taps in flight per work-item for CH >= 8
+#endif
+#ifndef VBM_PIPE_NARROW
+#define VBM_PIPE_NARROW 4  // taps in flight per work-item for CH < 8
+#endif
+#ifndef VBM_XCD_REMAP
+#define VBM_XCD_REMAP 1    // 1: give each of the 8 XCDs a contiguous range of blocks
+#endif
+#ifndef VBM_PIPE_SPLIT
+#define VBM_PIPE_SPLIT 8   // taps in flight per work-item in the split-row kernel
+#endif
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  With VBM_XCD_REMAP the workgroup id is mapped so that XCD k works on
+// the contiguous block range [k * per, (k + 1) * per): neighbouring blocks
+// share halo rows through one L2.  Returns n_blocks or more for padding
+// workgroups (they exit).
+__device__ __forceinline__ uint32_t block_of_workgroup(uint32_t wg, uint32_t n_blocks) {
+#if VBM_XCD_REMAP
+  const uint32_t per = (n_blocks + 7) / 8;
+  return (wg % 8) * per + wg / 8;
+#else
+  (void)n_blocks;
+  return wg;
+#endif
+}
+
+__host__ __device__ constexpr uint32_t box_grid_size(uint32_t n_blocks) {
+#if VBM_XCD_REMAP
+  return ((n_blocks + 7) / 8) * 8;
+#else
+  return n_blocks;
+#endif
+}
+
 // Dynamic LDS of the brick-cached kernels: the neighbour table of up to `cap`
 // spanned leaves, then their bricks.
 __host__ __device__ constexpr uint32_t brick_lds_bytes(uint32_t cap) { return cap * 27 * 4 + cap * kBrickCells * 4; }
@@ -253,7 +290,7 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
 template <int CH, bool VEC, bool STREAM>
 __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                    float* __restrict__ out, uint32_t C, uint32_t ch0) {
-  constexpr int kPipe = CH >= 8 ? 2 : 4;  // taps in flight per work-item
+  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
@@ -281,11 +318,12 @@ __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __
 template <int CH, bool VEC, bool STREAM>
 __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                     float* __restrict__ out, uint32_t C, uint32_t ch0, uint32_t cap) {
-  constexpr int kPipe = CH >= 8 ? 2 : 4;  // taps in flight per work-item
+  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
   extern __shared__ uint32_t lds[];
   uint32_t* table = lds;
   uint32_t* brick = lds + cap * 27;
-  const uint32_t b = blockIdx.x;
+  const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
+  if (b >= g.n_blocks) return;  // padding workgroup
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
@@ -325,6 +363,89 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
   if (!valid) return;
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   store_row<CH, VEC>(out + idx * C + ch0, acc);
+}
+
+// 27-tap box filter through the brick cache with each sidecar row split over
+// LANES = CH / 4 work-items (one float4 of channels each): a wave gathers
+// 64 / LANES whole rows per load instead of one 16-byte piece of 64 rows, and
+// writes whole output rows.  Slots are decoded once into LDS; the workgroup
+// has min(W * LANES, 1024) work-items, each handling W * LANES / blockDim
+// (slot, quarter) tasks.  Taps are streamed from the brick in tap order.
+template <int CH>
+__global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const float* __restrict__ sc,
+                                                           uint32_t sc_bytes, float* __restrict__ out, uint32_t C,
+                                                           uint32_t ch0, uint32_t cap) {
+  static_assert(CH % 4 == 0 && CH >= 8, "split rows need whole float4 groups");
+  constexpr uint32_t LANES = CH / 4;
+  constexpr int kPipe = VBM_PIPE_SPLIT;
+  extern __shared__ uint32_t lds[];
+  const uint32_t W = 1u << g.log2w;
+  uint32_t* slot_corner = lds;             // per slot: brick corner (cell index) | leaf-in-block << 16
+  uint32_t* table = lds + W;
+  uint32_t* brick = table + cap * 27;
+  const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
+  if (b >= g.n_blocks) return;  // padding workgroup
+  if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const uint32_t first = g.block_first_leaf[b];
+  const uint32_t span = block_span(g, b);  // block-uniform: every barrier below is uniform
+  const uint32_t tasks = W * LANES;
+  // one (slot, quarter) task: gather its 27 taps through off(t) and store
+  auto run = [&](uint32_t task, auto&& off) {
+    const uint32_t slot = task / LANES, q = task % LANES;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    gather_box_pipelined<4, true, kPipe>(acc, side, [&](int t) {
+      const uint32_t o = off(t);
+      return o == kInactive ? o : o + 16 * q;
+    });
+    const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + slot;
+    reinterpret_cast<float4*>(out + idx * C + ch0)[q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  // Phase 1: the waves holding slots decode them (lane-rank decode; a slot
+  // past the last index is marked 0xFFFFFFFF) while the other waves stage the
+  // neighbour table of the first pass, so the two chains of dependent loads
+  // overlap.
+  const bool cached = span <= kMaxCachedLeaves;
+  const uint32_t count0 = cached ? min(cap, span) : 0u;
+  if (threadIdx.x < W) {
+    const Slot s = decode_own_slot(g, b);
+    slot_corner[threadIdx.x] =
+        s.leaf == kSentinelLeaf
+            ? 0xFFFFFFFFu
+            : ((s.leaf - first) << 16) | ((s.offset >> 6) * 100 + ((s.offset >> 3) & 7) * 10 + (s.offset & 7));
+  }
+  const uint32_t stagers = blockDim.x > W ? blockDim.x - W : blockDim.x;
+  const uint32_t stager = blockDim.x > W ? threadIdx.x - W : threadIdx.x;  // wraps for decoders when blockDim > W
+  if (blockDim.x == W || threadIdx.x >= W) fill_table_range(g, first, count0, table, stager, stagers);
+  __syncthreads();
+  if (!cached) {  // per-tap tree walk
+    for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
+      const uint32_t info = slot_corner[task / LANES];
+      if (info == 0xFFFFFFFFu) continue;
+      const Leaf& L = g.leaves[first + (info >> 16)];
+      const uint32_t cell = info & 0xFFFF;
+      const int x = L.origin[0] + int(cell / 100), y = L.origin[1] + int((cell / 10) % 10);
+      const int z = L.origin[2] + int(cell % 10);
+      run(task, [&](int t) { return tap_offset(side, resolve_tree(g, x + box_di(t), y + box_dj(t), z + box_dk(t))); });
+    }
+    return;
+  }
+  for (uint32_t j0 = 0; j0 < span; j0 += cap) {
+    const uint32_t count = min(cap, span - j0);
+    if (j0) {  // later passes: the whole block restages
+      __syncthreads();  // the previous pass is done with the LDS
+      fill_table_range(g, first + j0, count, table, threadIdx.x, blockDim.x);
+      __syncthreads();
+    }
+    build_bricks(g, table, count, side.row_bytes, kInactive, brick);
+    for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
+      const uint32_t info = slot_corner[task / LANES];
+      const uint32_t j = info >> 16;
+      if (info == 0xFFFFFFFFu || j - j0 >= count) continue;
+      const uint32_t* corner = brick + (j - j0) * kBrickCells + (info & 0xFFFF);
+      run(task, [&](int t) { return corner[box_brick_offset(t)]; });
+    }
+  }
 }
 
 // 7-tap cross filter: sum, or 7-point Laplacian (faces in cross order) - fl(6 c).
@@ -432,16 +553,30 @@ int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out,
 
 // Brick capacity (spanned leaves resolved per pass) for BlockWidth 2^log2w:
 // one pass covers about 98% of the blocks of a sphere shell.
-uint32_t brick_capacity(int log2w) { return log2w <= 6 ? 3u : log2w == 7 ? 4u : log2w == 8 ? 6u : 8u; }
+#ifndef VBM_CAP_W128
+#define VBM_CAP_W128 4
+#endif
+#ifndef VBM_CAP_W512
+#define VBM_CAP_W512 8
+#endif
+uint32_t brick_capacity(int log2w) {
+  return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_CAP_W128) : log2w == 8 ? 6u : uint32_t(VBM_CAP_W512);
+}
 
 template <bool CACHED, bool STREAM>
 struct BoxLauncher {
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
-    if constexpr (CACHED) {
+    if constexpr (CACHED && VEC && STREAM && (CH == 8 || CH == 16)) {
       const uint32_t cap = brick_capacity(g.log2w);
-      hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w),
+      const uint32_t W = 1u << g.log2w;
+      const uint32_t threads = W * (CH / 4) < 1024 ? W * (CH / 4) : 1024;
+      hipLaunchKernelGGL((k_box_cached_split<CH>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
+                         brick_lds_bytes(cap) + W * 4, st, g, sc, bytes, out, C, ch0, cap);
+    } else if constexpr (CACHED) {
+      const uint32_t cap = brick_capacity(g.log2w);
+      hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(1u << g.log2w),
                          brick_lds_bytes(cap), st, g, sc, bytes, out, C, ch0, cap);
     } else {
       hipLaunchKernelGGL((k_box_plain<CH, VEC, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc,

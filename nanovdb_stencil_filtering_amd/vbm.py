@@ -122,7 +122,7 @@ def blob_sections(hdr: GridHeader, blob: np.ndarray) -> dict:
     """Numpy views of the blob's sections (layout of include/vbm.h)."""
     L, nb, W = hdr.n_leaves, hdr.n_blocks, 1 << hdr.log2_width
     leaf_dt = np.dtype([("mask", "<u8", (8,)), ("prefix", "<u8"), ("first", "<u8"), ("origin", "<i4", (3,)),
-                        ("pad", "<u4", (9,))])
+                        ("lower", "<u4"), ("upper", "<u4"), ("pad", "<u4", (7,))])
     root_dt = np.dtype([("key", "<i4", (3,)), ("upper", "<u4")])
 
     def sec(off, dt, count):

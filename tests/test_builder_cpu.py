@@ -64,6 +64,8 @@ def test_tree_nodes_reach_every_leaf(pair):
         lower = s["upper"][up, ((x >> 7) & 31) << 10 | ((y >> 7) & 31) << 5 | ((z >> 7) & 31)]
         assert lower != 0xFFFFFFFF
         assert s["lower"][lower, ((x >> 3) & 15) << 8 | ((y >> 3) & 15) << 4 | ((z >> 3) & 15)] == l
+        # parent ids kept in the leaf record
+        assert s["leaves"]["lower"][l] == lower and s["leaves"]["upper"][l] == up
     # every non-empty lower slot is a leaf, every non-empty upper slot a lower node
     assert int((s["lower"] != 0xFFFFFFFF).sum()) == hdr.n_leaves
     assert int((s["upper"] != 0xFFFFFFFF).sum()) == hdr.n_lower
