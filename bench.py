@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+PROFILE = os.path.join(ROOT, "profiles", "box_cached_streaming_cfg_shell_C16_W128.txt")
 
 
 def log(msg):
@@ -48,6 +49,40 @@ def alg_bytes_decode(n_active, n_leaves, n_blocks, width):
     """Decode: 6 B written per slot (u32 + u16), leaf mask/prefix/first (80 B),
     block metadata."""
     return 6 * n_blocks * width + 80 * n_leaves + (4 + width // 8) * n_blocks
+
+
+def kernel_sources_sha256():
+    """Hash of the kernel sources; the HBM counters in profiles/ are valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("vbm_device.hpp", "vbm_kernels.hip"):
+        with open(os.path.join(ROOT, "nanovdb_stencil_filtering_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(path=PROFILE):
+    """HBM bytes per launch of the headline kernel from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    summarised in profiles/ (already scaled by the copy calibration), or None when the summary is
+    missing or was taken on other kernel sources."""
+    try:
+        with open(path) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line)
+    except OSError:
+        return None
+    if kv.get("sources_sha256", "").strip() != kernel_sources_sha256():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"].split()[0])
+    except (KeyError, ValueError):
+        return None
+
+
+def headline_kernel(channels):
+    """Name of the kernel vbm_box_filter launches for the cached streaming box at these channels."""
+    if channels in (8, 16):
+        return "k_box_cached_split<%d>" % channels
+    return "k_box_cached<%d,%s,true>" % (channels, "true" if channels % 4 == 0 else "false")
 
 
 def time_launches(fn, n_sets, steps, warmup):
@@ -190,6 +225,8 @@ def main():
             t = time_launches(dec, 4, 50, 15)
             rec("decode_W%d" % gw.width, t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
 
+    traffic = counted_traffic() if (C == 16 and W == 128) else None
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -226,8 +263,8 @@ def main():
                    "n_active": N, "n_leaves": L, "block_width": W, "channels": C,
                    "buffer_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": ab, "kernel": "k_box<16,true,true,true>"},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": ab, "kernel": headline_kernel(C)},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -94,7 +94,7 @@ BOX_FLAGS = [0, vbm.STREAMING, vbm.CACHED, vbm.CACHED | vbm.STREAMING]
 
 
 @pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube"])
 def test_box_filter(name, C):
     for log2w in (7, 9):
         g, ref = grid_pair(name, log2w)
