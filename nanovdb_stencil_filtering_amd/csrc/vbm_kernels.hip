@@ -160,6 +160,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_XCD_REMAP
 #define VBM_XCD_REMAP 1    // 1: give each of the 8 XCDs a contiguous range of blocks
 #endif
+#ifndef VBM_SPLIT_MAX
+#define VBM_SPLIT_MAX 256  // work-items per workgroup of the split-row kernel (at least W)
+#endif
 #ifndef VBM_PIPE_SPLIT
 #define VBM_PIPE_SPLIT 8   // taps in flight per work-item in the split-row kernel
 #endif
@@ -571,7 +574,8 @@ struct BoxLauncher {
     if constexpr (CACHED && VEC && STREAM && (CH == 8 || CH == 16)) {
       const uint32_t cap = brick_capacity(g.log2w);
       const uint32_t W = 1u << g.log2w;
-      const uint32_t threads = W * (CH / 4) < 1024 ? W * (CH / 4) : 1024;
+      const uint32_t tasks = W * (CH / 4);
+      const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
       hipLaunchKernelGGL((k_box_cached_split<CH>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
                          brick_lds_bytes(cap) + W * 4, st, g, sc, bytes, out, C, ch0, cap);
     } else if constexpr (CACHED) {
