@@ -67,6 +67,8 @@ def _load():
     lib.oracle_box_filter.argtypes = [P, P, I32, P]
     lib.oracle_cross_filter.restype = I32
     lib.oracle_cross_filter.argtypes = [P, P, I32, I32, P]
+    lib.oracle_axis_rows.argtypes = [P, P, I32, P, I64, P]
+    lib.oracle_axis_filter.argtypes = [P, P, I32, P]
     _lib = lib
     return lib
 
@@ -132,7 +134,7 @@ class OracleGrid:
         idx = np.ascontiguousarray(idx, dtype=np.uint64)
         out = np.empty((idx.size, shape), np.uint64)
         if self._lib.oracle_taps_rows(self._h, shape, _ptr(idx), idx.size, _ptr(out)) != 0:
-            raise ValueError("shape must be 27 or 7")
+            raise ValueError("shape must be 27, 7 or 19")
         return out
 
     def box(self, sidecar: np.ndarray, idx: np.ndarray | None = None) -> np.ndarray:
@@ -160,4 +162,18 @@ class OracleGrid:
         idx = np.ascontiguousarray(idx, dtype=np.uint64)
         out = np.empty((idx.size, C), np.float32)
         self._lib.oracle_cross_rows(self._h, _ptr(sc), C, code, _ptr(idx), idx.size, _ptr(out))
+        return out
+
+    def axis(self, sidecar: np.ndarray, idx: np.ndarray | None = None) -> np.ndarray:
+        """19-tap axis stencil (centre and +-1..+-3 along each axis): fp32 sum in tap order."""
+        sc = np.ascontiguousarray(sidecar, dtype=np.float32)
+        C = sc.shape[1]
+        assert sc.shape[0] == self.n_active + 1
+        if idx is None:
+            out = np.empty((self.n_active + 1, C), np.float32)
+            self._lib.oracle_axis_filter(self._h, _ptr(sc), C, _ptr(out))
+            return out
+        idx = np.ascontiguousarray(idx, dtype=np.uint64)
+        out = np.empty((idx.size, C), np.float32)
+        self._lib.oracle_axis_rows(self._h, _ptr(sc), C, _ptr(idx), idx.size, _ptr(out))
         return out

@@ -8,6 +8,10 @@
 // every fp32 operation is one IEEE round-to-nearest-even step.
 //
 // Sources (the pages):
+//  * openvdb PR #2258 "VBM select-based inverse-map decode", "A/B": the 7-point
+//    Laplacian, the 27-tap box and a 19-tap WENO consumer as the downstream
+//    stencil consumers; the 19-tap shape is the centre plus three voxels each
+//    way along every axis (the reach of a fifth-order WENO stencil).
 //  * openvdb PR #2262 "NanoVDB VBM: Streaming box-stencil", section "What
 //    changed": in an index grid a stencil resolves to indices, index 0 means
 //    "no active voxel" and is skipped, a filter gathers sidecar[index*C + ch]
@@ -41,6 +45,9 @@
 //  * decode sentinels: leafIndex 0xFFFFFFFF, voxelOffset 0xFFFF;
 //  * di runs along x, dj along y, dk along z;
 //  * cross taps: the box taps with |di|+|dj|+|dk| <= 1 in ascending box order;
+//  * 19-tap axis stencil: the offsets with at most one nonzero component of
+//    magnitude <= 3, in ascending lexicographic (di, dj, dk) order (centre = 9);
+//    its consumer accumulates the 19 taps like the box and cross consumers;
 //  * box filter = plain sum (no division); cross sum = sum over 7 taps;
 //    7-point Laplacian = (sum of the active face taps, in cross order) minus
 //    the separately rounded product 6*centre.
@@ -111,16 +118,28 @@ std::vector<int> cross_taps() {
   return taps;
 }
 
+// The 19 axis offsets: at most one nonzero component, of magnitude <= 3, in
+// ascending lexicographic (di, dj, dk) order.
+std::vector<Coord> axis19_offsets() {
+  std::vector<Coord> v;
+  for (int di = -3; di <= 3; ++di)
+    for (int dj = -3; dj <= 3; ++dj)
+      for (int dk = -3; dk <= 3; ++dk)
+        if ((di != 0) + (dj != 0) + (dk != 0) <= 1) v.push_back({di, dj, dk});
+  return v;
+}
+
 uint64_t lookup(const Grid& g, const Coord& q) {
   auto it = g.index.find(pack(q));
   return it == g.index.end() ? 0 : it->second;
 }
 
-uint64_t tap_index(const Grid& g, uint64_t idx, int t) {
+uint64_t offset_index(const Grid& g, uint64_t idx, const Coord& d) {
   const Coord& p = g.voxel[idx - 1];
-  Coord d = box_offset(t);
   return lookup(g, Coord{p.x + d.x, p.y + d.y, p.z + d.z});
 }
+
+uint64_t tap_index(const Grid& g, uint64_t idx, int t) { return offset_index(g, idx, box_offset(t)); }
 
 int64_t n_blocks(int64_t n_active, int log2w) {
   int64_t w = int64_t(1) << log2w;
@@ -262,20 +281,39 @@ void oracle_decode(const void* h, int log2w, uint32_t* leaf_index, uint16_t* vox
 }
 
 // Raw stencil taps for the m indices in idx[]: taps[i*shape + j] = index of
-// tap j of voxel idx[i] (0 = inactive).  shape 27 = box, 7 = cross.
+// tap j of voxel idx[i] (0 = inactive).  shape 27 = box, 7 = cross, 19 = axis.
 int oracle_taps_rows(const void* h, int shape, const uint64_t* idx, int64_t m, uint64_t* taps) {
   const Grid& g = *static_cast<const Grid*>(h);
-  std::vector<int> order;
+  std::vector<Coord> offsets;
   if (shape == 27) {
-    for (int t = 0; t < 27; ++t) order.push_back(t);
+    for (int t = 0; t < 27; ++t) offsets.push_back(box_offset(t));
   } else if (shape == 7) {
-    order = cross_taps();
+    for (int t : cross_taps()) offsets.push_back(box_offset(t));
+  } else if (shape == 19) {
+    offsets = axis19_offsets();
   } else {
     return -1;
   }
   for (int64_t i = 0; i < m; ++i)
-    for (int j = 0; j < shape; ++j) taps[i * shape + j] = tap_index(g, idx[i], order[size_t(j)]);
+    for (int j = 0; j < shape; ++j) taps[i * shape + j] = offset_index(g, idx[i], offsets[size_t(j)]);
   return 0;
+}
+
+// 19-tap axis filter for the m indices in idx[]: out[i*C + ch] = fp32 sum, in
+// tap order, of sidecar[tap*C + ch] over the active taps of voxel idx[i].
+void oracle_axis_rows(const void* h, const float* sidecar, int C, const uint64_t* idx, int64_t m, float* out) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  const std::vector<Coord> offsets = axis19_offsets();
+  for (int64_t i = 0; i < m; ++i) {
+    uint64_t tap[19];
+    for (int j = 0; j < 19; ++j) tap[j] = offset_index(g, idx[i], offsets[size_t(j)]);
+    for (int ch = 0; ch < C; ++ch) {
+      float acc = 0.0f;
+      for (int j = 0; j < 19; ++j)
+        if (tap[j]) acc += sidecar[tap[j] * uint64_t(C) + uint64_t(ch)];
+      out[i * C + ch] = acc;
+    }
+  }
 }
 
 // Box filter for the m indices in idx[]: out[i*C + ch] = fp32 sum, in tap
@@ -335,6 +373,14 @@ int oracle_cross_filter(const void* h, const float* sidecar, int C, int op, floa
   std::vector<uint64_t> idx(static_cast<size_t>(N));
   for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
   return oracle_cross_rows(h, sidecar, C, op, idx.data(), N, out + C);
+}
+
+void oracle_axis_filter(const void* h, const float* sidecar, int C, float* out) {
+  const int64_t N = oracle_n_active(h);
+  for (int ch = 0; ch < C; ++ch) out[ch] = 0.0f;
+  std::vector<uint64_t> idx(static_cast<size_t>(N));
+  for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
+  oracle_axis_rows(h, sidecar, C, idx.data(), N, out + C);
 }
 
 }  // extern "C"
