@@ -200,30 +200,34 @@ def main():
             for w in (7, 9):
                 gw = grids[w]
                 if ch in (1, 8):
-                    for cached in (0, vbm.CACHED):
-                        t = time_launches(lambda k: vbm.cross_filter(gw, s_[k], cached | vbm.OP_LAPLACIAN,
-                                                                     out=o_[k]), ns_, 20, 5)
-                        rec("laplacian_%s_W%d_C%d" % ("cached" if cached else "plain", gw.width, ch), t,
-                            alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch), N * ch)
+                    ab_w = alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch)
+                    for fl, nm in names.items():
+                        t = time_launches(lambda k: vbm.cross_filter(gw, s_[k], fl | vbm.OP_LAPLACIAN, out=o_[k]),
+                                          ns_, 20, 5)
+                        rec("laplacian_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
+                    for fl, nm in names.items():
+                        t = time_launches(lambda k: vbm.axis_filter(gw, s_[k], fl, out=o_[k]), ns_, 20, 5)
+                        rec("axis19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
             if ch != C:
                 del s_, o_
         # hot-cache figure (single buffer set; the Infinity Cache may serve it)
         t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
         rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
-        for w in (7, 9):
-            gw = grids[w]
+        # decode: select-based vs the sweep it replaced, every width (the pages' A/B)
+        lib = vbm.load_library()
+        import ctypes
+        for w in (6, 7, 8, 9):
+            gw = grids[w] if w in grids else vbm.build(coords, w, device=dev)
             lo = [torch.empty(gw.n_slots, dtype=torch.int32, device=dev) for _ in range(4)]
             oo = [torch.empty(gw.n_slots, dtype=torch.int16, device=dev) for _ in range(4)]
-            lib = vbm.load_library()
-            import ctypes
-
-            def dec(k, gw=gw, lo=lo, oo=oo):
-                rc = lib.vbm_decode(ctypes.byref(gw.hdr), ctypes.c_void_p(gw.blob.data_ptr()),
-                                    ctypes.c_void_p(lo[k].data_ptr()), ctypes.c_void_p(oo[k].data_ptr()),
-                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                assert rc == 0
-            t = time_launches(dec, 4, 50, 15)
-            rec("decode_W%d" % gw.width, t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
+            for fn, nm in ((lib.vbm_decode, "decode"), (lib.vbm_decode_sweep, "decode_sweep")):
+                def dec(k, gw=gw, lo=lo, oo=oo, fn=fn):
+                    rc = fn(ctypes.byref(gw.hdr), ctypes.c_void_p(gw.blob.data_ptr()),
+                            ctypes.c_void_p(lo[k].data_ptr()), ctypes.c_void_p(oo[k].data_ptr()),
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    assert rc == 0
+                t = time_launches(dec, 4, 50, 15)
+                rec("%s_W%d" % (nm, gw.width), t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
 
     traffic = counted_traffic() if (C == 16 and W == 128) else None
 

@@ -10,7 +10,7 @@
  *             select into the leaf's value mask through its prefix directory
  *             (openvdb PR #2258, "VBM select-based inverse-map decode",
  *             "Summary" and "What changed");
- *   resolve   the 27-tap box and 7-tap cross stencils to indices, by a
+ *   resolve   the 27-tap box, 7-tap cross and 19-tap axis stencils to indices, by a
  *             root-down tree walk per tap or through a per-block table of
  *             neighbour leaves staged in LDS (openvdb PR #2263, "Alternative
  *             stencil resolvers for VoxelBlockManager", "Summary");
@@ -50,13 +50,13 @@ typedef enum vbm_status {
   VBM_ERR_ALIAS = -4,       /* output overlaps the sidecar (neighbours are read while writing) */
   VBM_ERR_RANGE = -5,       /* coordinate with |c| >= 2^30                                      */
   VBM_ERR_HIP = -6,         /* a HIP launch failed                                              */
-  VBM_ERR_UNSUPPORTED = -7, /* a combination the library does not offer                         */
+  VBM_ERR_UNSUPPORTED = -7, /* a combination the library does not offer (reserved)              */
   VBM_ERR_NOMEM = -8        /* host allocation in vbm_build failed                              */
 } vbm_status;
 
 /* flags */
 #define VBM_CACHED 0x1        /* resolve through the LDS neighbour-leaf table (else tree walk)  */
-#define VBM_STREAMING 0x2     /* box only: stream taps to the consumer (else materialise 27)   */
+#define VBM_STREAMING 0x2     /* stream taps to the consumer (else materialise them first)     */
 #define VBM_OP_SUM 0x0        /* cross filter: sum of the 7 taps                                */
 #define VBM_OP_LAPLACIAN 0x4  /* cross filter: (sum of active faces) - 6*centre                 */
 
@@ -141,16 +141,31 @@ int vbm_decode(const vbm_grid* grid, const void* d_blob, uint32_t* d_leaf_index,
                void* stream);
 
 /*
+ * Inverse-map decode by the sweep that the select-based decode replaced
+ * (openvdb PR #2258, "Summary": every thread of a block swept all 512 voxel
+ * positions of every leaf overlapping the block, O(nLeaves x 512) per block).
+ * Kept as the A/B baseline of the decode metric ("A/B" table of that page).
+ * Arguments, outputs, sentinels and errors exactly as vbm_decode; the maps are
+ * identical.
+ */
+int vbm_decode_sweep(const vbm_grid* grid, const void* d_blob, uint32_t* d_leaf_index, uint16_t* d_voxel_offset,
+                     void* stream);
+
+/*
  * Raw stencil taps of every slot (openvdb PR #2263, "Validation": all taps of
  * every thread written to global memory and compared bytewise).
- *   shape   27 (box, tap t = (di+1)*9 + (dj+1)*3 + (dk+1)) or 7 (cross: the box
- *           taps 4, 10, 12, 13, 14, 16, 22, i.e. -x, -y, -z, centre, +z, +y, +x)
- *   flags   VBM_CACHED and, for the box, VBM_STREAMING (taps are then written from
- *           the streaming callback instead of a materialised array)
+ *   shape   27 (box, tap t = (di+1)*9 + (dj+1)*3 + (dk+1)),
+ *           7 (cross: the box taps 4, 10, 12, 13, 14, 16, 22, i.e. -x, -y, -z,
+ *           centre, +z, +y, +x), or
+ *           19 (axis stencil, the reach of the 19-tap WENO consumer named in
+ *           openvdb PR #2258, "A/B": the centre and +-1..+-3 along each axis, in
+ *           ascending lexicographic (di, dj, dk) order; tap 9 = centre)
+ *   flags   VBM_CACHED (box: the LDS brick; cross and axis: the per-tap table
+ *           of the 7 leaf directions) and VBM_STREAMING (taps written from the
+ *           streaming callback instead of a materialised array)
  *   d_taps  device u64 [n_blocks * W * shape]: row b*W + s = taps of slot s of block b;
  *           0 = inactive neighbour; rows of sentinel slots are all 0
- * Errors: VBM_ERR_ARG, VBM_ERR_UNSUPPORTED (cross with VBM_STREAMING:
- * openvdb PR #2263, "Notes", has no streaming cross form), VBM_ERR_HIP.
+ * Errors: VBM_ERR_ARG, VBM_ERR_HIP.
  */
 int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int shape, int flags, uint64_t* d_taps,
                         void* stream);
@@ -176,12 +191,29 @@ int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_side
  *   VBM_OP_SUM        out = fp32 sum, in cross order from +0, over the active taps
  *   VBM_OP_LAPLACIAN  out = (fp32 sum over the active face taps in cross order)
  *                           - fl(6 * centre)
- *   flags: VBM_CACHED plus one op.  Taps are materialised (7 entries).
+ *   flags: VBM_CACHED, VBM_STREAMING and one op.  VBM_STREAMING streams the 7
+ *   taps into the gather (the forEachCrossStencil that openvdb PR #2263,
+ *   "Notes", leaves out as a wash on its hardware); without it the taps are
+ *   materialised (7 entries) first.  All forms give identical bits.
  * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
- * VBM_ERR_ALIAS, VBM_ERR_UNSUPPORTED (VBM_STREAMING), VBM_ERR_HIP.
+ * VBM_ERR_ALIAS, VBM_ERR_HIP.
  */
 int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                      int flags, void* stream);
+
+/*
+ * 19-tap axis filter: the stencil of the 19-tap WENO consumer (openvdb PR
+ * #2258, "A/B"), with its taps accumulated the way the pages' box and cross
+ * consumers accumulate theirs (openvdb PR #2263, "Measurements"):
+ *   out[g*C + ch] = fp32 sum, in axis tap order (see vbm_stencil_indices) from
+ *   +0, of sidecar[tap*C + ch] over the active taps of voxel g.
+ *   flags: VBM_CACHED (table of the 7 leaf directions: a reach of 3 < 8 leaves
+ *   the leaf in at most one axis) and VBM_STREAMING.  All forms give identical bits.
+ * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
+ * VBM_ERR_ALIAS, VBM_ERR_HIP.
+ */
+int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                    int flags, void* stream);
 
 /* Static English text for a status code. */
 const char* vbm_strerror(int status);

@@ -8,6 +8,7 @@
 //   for_each_box[_cached]  27 taps streamed to a callback in tap order
 //   compute_box[_cached]   27 taps materialised into an array
 //   compute_cross[_cached] 7 taps materialised into an array
+//   for_each_tap[_cached]  any shape (box, cross, 19-tap axis) streamed
 //
 // Sources: openvdb PR #2258 "VBM select-based inverse-map decode" ("What
 // changed": rank into the jumpMap, select into the value mask guided by the
@@ -260,6 +261,37 @@ __host__ __device__ constexpr int cross_box_tap(int j) {
   return j == 0 ? 4 : j == 1 ? 10 : j == 2 ? 12 : j == 3 ? 13 : j == 4 ? 14 : j == 5 ? 16 : 22;
 }
 
+// 19-tap axis stencil (the reach of a fifth-order WENO consumer): the centre
+// and +-1..+-3 along each axis, ascending lexicographic (di, dj, dk) order;
+// tap 9 is the centre.  A reach of 3 < 8 leaves the leaf in at most one axis,
+// so its cached table has the 7 directions of the cross.
+constexpr int kAxisTaps = 19;
+__host__ __device__ constexpr int axis_di(int j) { return j < 3 ? j - 3 : j >= 16 ? j - 15 : 0; }
+__host__ __device__ constexpr int axis_dj(int j) { return (j >= 3 && j < 6) ? j - 6 : (j >= 13 && j < 16) ? j - 12 : 0; }
+__host__ __device__ constexpr int axis_dk(int j) { return (j >= 6 && j < 13) ? j - 9 : 0; }
+
+// Stencil shapes: tap count, cached-table directions per leaf, offsets.
+struct BoxShape {
+  static constexpr int kTaps = kBoxTaps, kDirs = 27;
+  __host__ __device__ static constexpr int di(int t) { return box_di(t); }
+  __host__ __device__ static constexpr int dj(int t) { return box_dj(t); }
+  __host__ __device__ static constexpr int dk(int t) { return box_dk(t); }
+};
+struct CrossShape {
+  static constexpr int kTaps = kCrossTaps, kDirs = 7;
+  static constexpr int kCentre = 3;
+  __host__ __device__ static constexpr int di(int j) { return box_di(cross_box_tap(j)); }
+  __host__ __device__ static constexpr int dj(int j) { return box_dj(cross_box_tap(j)); }
+  __host__ __device__ static constexpr int dk(int j) { return box_dk(cross_box_tap(j)); }
+};
+struct AxisShape {
+  static constexpr int kTaps = kAxisTaps, kDirs = 7;
+  static constexpr int kCentre = 9;
+  __host__ __device__ static constexpr int di(int j) { return axis_di(j); }
+  __host__ __device__ static constexpr int dj(int j) { return axis_dj(j); }
+  __host__ __device__ static constexpr int dk(int j) { return axis_dk(j); }
+};
+
 // Leaf-level direction slot of a neighbour leaf in a table with DIRS entries
 // per spanned leaf.  Box: 27 directions in the same order as the box taps.
 // Cross: the 7 directions of the cross taps (a one-voxel reach in one axis
@@ -448,6 +480,25 @@ __device__ __forceinline__ void compute_box(const DeviceGrid& g, Slot s, uint64_
 __device__ __forceinline__ void compute_box_cached(const DeviceGrid& g, const uint32_t* table, uint32_t first_leaf,
                                                    Slot s, uint64_t (&st)[kBoxTaps]) {
   for_each_box_cached(g, table, first_leaf, s, [&](int t, uint32_t idx) { st[t] = idx; });
+}
+
+// Any shape: taps by tree walks, streamed to f(tap, index) in tap order.
+template <class S, class F>
+__device__ __forceinline__ void for_each_tap(const DeviceGrid& g, Slot s, F&& f) {
+  const VoxelCoord p = voxel_coord(g, s);
+#pragma unroll
+  for (int t = 0; t < S::kTaps; ++t) f(t, resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+}
+
+// Any shape: taps through the staged table of neighbour leaves (S::kDirs per
+// spanned leaf), streamed to f(tap, index) in tap order.
+template <class S, class F>
+__device__ __forceinline__ void for_each_tap_cached(const DeviceGrid& g, const uint32_t* table, uint32_t first_leaf,
+                                                    Slot s, F&& f) {
+  const uint32_t j = s.leaf - first_leaf;
+  const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+#pragma unroll
+  for (int t = 0; t < S::kTaps; ++t) f(t, resolve_cached<S::kDirs>(g, table, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
 }
 
 __device__ __forceinline__ void compute_cross(const DeviceGrid& g, Slot s, uint64_t (&st)[kCrossTaps]) {

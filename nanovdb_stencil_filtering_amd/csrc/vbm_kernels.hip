@@ -108,25 +108,25 @@ struct Row {
   }
 };
 
-// Gather-accumulate of the 27 box taps in tap order, software pipelined:
+// Gather-accumulate of NT taps (default: the 27 box taps) in tap order, software pipelined:
 // the rows of taps t+1..t+D are in flight while tap t is added, and the
 // scheduler is fenced between steps so it cannot hoist all 27 rows at once
 // (which costs more registers than a wave can hold).  off(t) gives the byte
 // offset of tap t (kInactive for an inactive tap).
-template <int CH, bool VEC, int D, class Off>
+template <int CH, bool VEC, int D, int NT = kBoxTaps, class Off>
 __device__ __forceinline__ void gather_box_pipelined(float (&acc)[CH], const Sidecar& s, Off&& off) {
   Row<CH, VEC> buf[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) buf[t].load(s, off(t));
 #pragma unroll
-  for (int t = 0; t < kBoxTaps; ++t) {
+  for (int t = 0; t < NT; ++t) {
     __builtin_amdgcn_sched_barrier(0);
     buf[t % D].add_to(acc);
     // Keep tap t's adds here: without this the compiler sinks every add below
-    // the tree walks of later taps and keeps all 27 rows live.  Emits nothing.
+    // the tree walks of later taps and keeps all the rows live.  Emits nothing.
 #pragma unroll
     for (int c = 0; c < CH; ++c) asm volatile("" : "+v"(acc[c]));
-    if (t + D < kBoxTaps) buf[t % D].load(s, off(t + D));
+    if (t + D < NT) buf[t % D].load(s, off(t + D));
   }
 }
 
@@ -206,6 +206,37 @@ __global__ void __launch_bounds__(512) k_decode(DeviceGrid g, uint32_t* __restri
   voxel_offset[row] = uint16_t(s.offset);
 }
 
+// Inverse maps by the sweep that the select-based decode replaced
+// (openvdb PR #2258, "Summary"): the workgroup of block b walks every voxel
+// position of every leaf the block spans, O(span x 512) per block; a set bit
+// whose index falls inside the block writes its slot.  Slots past the last
+// active index receive the sentinels.  Same maps as k_decode.
+__global__ void __launch_bounds__(512) k_decode_sweep(DeviceGrid g, uint32_t* __restrict__ leaf_index,
+                                                      uint16_t* __restrict__ voxel_offset) {
+  const uint32_t b = blockIdx.x;
+  const uint32_t W = 1u << g.log2w;
+  const uint64_t g0 = 1 + (uint64_t(b) << g.log2w);
+  uint32_t* li = leaf_index + (uint64_t(b) << g.log2w);
+  uint16_t* vo = voxel_offset + (uint64_t(b) << g.log2w);
+  if (g0 + threadIdx.x > g.n_active) {
+    li[threadIdx.x] = kSentinelLeaf;
+    vo[threadIdx.x] = uint16_t(kSentinelOffset);
+  }
+  const uint32_t first = g.block_first_leaf[b];
+  const uint32_t span = block_span(g, b);
+  for (uint32_t j = 0; j < span; ++j) {
+    const Leaf& L = g.leaves[first + j];
+    for (uint32_t o = threadIdx.x; o < 512; o += blockDim.x) {
+      const uint32_t idx = index_in_leaf(L, o);  // 0 if the position is inactive
+      const uint64_t slot = uint64_t(idx) - g0;
+      if (idx != 0 && slot < W) {
+        li[slot] = first + j;
+        vo[slot] = uint16_t(o);
+      }
+    }
+  }
+}
+
 // Raw box taps through the brick cache (materialised or streamed), block by
 // block in passes of at most `cap` spanned leaves; blocks spanning more than
 // kMaxCachedLeaves walk the tree per tap.
@@ -248,44 +279,42 @@ __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t*
   }
 }
 
-// Raw taps by the tree walk (box or cross) and by the per-tap cached table (cross).
-template <int SHAPE, bool CACHED, bool STREAM>
+// Raw taps of any shape by tree walks, or of the 7-direction shapes (cross,
+// 19-tap axis) through the per-tap cached table of neighbour leaves; streamed
+// straight to the output row or materialised into an array first.
+template <class S, bool CACHED, bool STREAM>
 __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict__ taps) {
-  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * SHAPE : 1];
+  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * S::kDirs : 1];
   const uint32_t b = blockIdx.x;
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
-  uint64_t* out = taps + ((uint64_t(b) << g.log2w) + threadIdx.x) * SHAPE;
+  uint64_t* out = taps + ((uint64_t(b) << g.log2w) + threadIdx.x) * S::kTaps;
   bool cached = false;
   uint32_t first = 0;
   if constexpr (CACHED) {
     first = g.block_first_leaf[b];
     const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
     if (span <= kMaxCachedLeaves) {
-      stage_neighbour_table<SHAPE>(g, first, span, table);
+      stage_neighbour_table<S::kDirs>(g, first, span, table);
       cached = true;
     }
   }
   if (!valid) {
 #pragma unroll
-    for (int j = 0; j < SHAPE; ++j) out[j] = 0;
+    for (int j = 0; j < S::kTaps; ++j) out[j] = 0;
     return;
   }
-  if constexpr (SHAPE == 27) {
-    if constexpr (STREAM) {
-      for_each_box(g, s, [&](int t, uint32_t idx) { out[t] = idx; });
-    } else {
-      uint64_t st[kBoxTaps];
-      compute_box(g, s, st);
-#pragma unroll
-      for (int t = 0; t < kBoxTaps; ++t) out[t] = st[t];
-    }
+  if constexpr (STREAM) {
+    auto put = [&](int t, uint32_t idx) { out[t] = idx; };
+    if (cached) for_each_tap_cached<S>(g, table, first, s, put);
+    else for_each_tap<S>(g, s, put);
   } else {
-    uint64_t st[kCrossTaps];
-    if (cached) compute_cross_cached(g, table, first, s, st);
-    else compute_cross(g, s, st);
+    uint64_t st[S::kTaps];
+    auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
+    if (cached) for_each_tap_cached<S>(g, table, first, s, keep);
+    else for_each_tap<S>(g, s, keep);
 #pragma unroll
-    for (int j = 0; j < kCrossTaps; ++j) out[j] = st[j];
+    for (int j = 0; j < S::kTaps; ++j) out[j] = st[j];
   }
 }
 
@@ -451,11 +480,15 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   }
 }
 
-// 7-tap cross filter: sum, or 7-point Laplacian (faces in cross order) - fl(6 c).
-template <int CH, bool VEC, bool CACHED, bool LAP>
-__global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
-                                               float* __restrict__ out, uint32_t C, uint32_t ch0) {
-  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * kCrossTaps : 1];
+// Filters of the 7-direction shapes: the cross (sum, or 7-point Laplacian =
+// faces in cross order - fl(6 c)) and the 19-tap axis stencil (sum).  Taps by
+// tree walks or through the per-tap cached table; streamed into the gather
+// pipeline (STREAM) or materialised into an array first.
+template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM>
+__global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                                 float* __restrict__ out, uint32_t C, uint32_t ch0) {
+  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
+  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * S::kDirs : 1];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
@@ -464,24 +497,43 @@ __global__ void __launch_bounds__(512) k_cross(DeviceGrid g, const float* __rest
   uint32_t first = 0;
   if constexpr (CACHED) {
     first = g.block_first_leaf[b];
-    const uint32_t span = block_span(g, b);
+    const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
     if (span <= kMaxCachedLeaves) {
-      stage_neighbour_table<kCrossTaps>(g, first, span, table);
+      stage_neighbour_table<S::kDirs>(g, first, span, table);
       cached = true;
     }
   }
   if (!valid) return;
   const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
-  uint64_t st[kCrossTaps];
-  if (cached) compute_cross_cached(g, table, first, s, st);
-  else compute_cross(g, s, st);
   float acc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+  // the Laplacian's centre enters only as -6 * centre: it reads as an inactive tap here
+  if constexpr (STREAM) {
+    if (cached) {
+      const uint32_t j = s.leaf - first;
+      const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+      gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
+        if (LAP && t == S::kCentre) return kInactive;
+        return tap_offset(side, resolve_cached<S::kDirs>(g, table, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+      });
+    } else {
+      const VoxelCoord p = voxel_coord(g, s);
+      gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
+        if (LAP && t == S::kCentre) return kInactive;
+        return tap_offset(side, resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+      });
+    }
+  } else {
+    uint64_t st[S::kTaps];
+    auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
+    if (cached) for_each_tap_cached<S>(g, table, first, s, keep);
+    else for_each_tap<S>(g, s, keep);
 #pragma unroll
-  for (int j = 0; j < kCrossTaps; ++j) {
-    if (LAP && j == 3) continue;  // the centre enters the Laplacian only as -6*centre
-    add_row<CH, VEC>(acc, side, tap_offset(side, uint32_t(st[j])));
+    for (int j = 0; j < S::kTaps; ++j) {
+      if (LAP && j == S::kCentre) continue;
+      add_row<CH, VEC>(acc, side, tap_offset(side, uint32_t(st[j])));
+    }
   }
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   if constexpr (LAP) {
@@ -589,13 +641,13 @@ struct BoxLauncher {
   }
 };
 
-template <bool CACHED, bool LAP>
-struct CrossLauncher {
+template <class S, bool CACHED, bool LAP, bool STREAM>
+struct StencilLauncher {
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
-    hipLaunchKernelGGL((k_cross<CH, VEC, CACHED, LAP>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc,
-                       bytes, out, C, ch0);
+    hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g,
+                       sc, bytes, out, C, ch0);
   }
 };
 
@@ -652,13 +704,24 @@ extern "C" int vbm_decode(const vbm_grid* grid, const void* d_blob, uint32_t* d_
   return launch_status();
 }
 
+extern "C" int vbm_decode_sweep(const vbm_grid* grid, const void* d_blob, uint32_t* d_leaf_index,
+                                uint16_t* d_voxel_offset, void* stream) {
+  int rc = check_grid(grid, d_blob);
+  if (rc) return rc;
+  if (grid->n_blocks == 0) return VBM_OK;
+  if (!d_leaf_index || !d_voxel_offset) return VBM_ERR_ARG;
+  const DeviceGrid g = device_grid(grid, d_blob);
+  hipLaunchKernelGGL(k_decode_sweep, dim3(g.n_blocks), dim3(1u << g.log2w), 0, static_cast<hipStream_t>(stream), g,
+                     d_leaf_index, d_voxel_offset);
+  return launch_status();
+}
+
 extern "C" int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int shape, int flags, uint64_t* d_taps,
                                    void* stream) {
   int rc = check_grid(grid, d_blob);
   if (rc) return rc;
-  if (shape != 27 && shape != 7) return VBM_ERR_ARG;
+  if (shape != 27 && shape != 7 && shape != 19) return VBM_ERR_ARG;
   if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
-  if (shape == 7 && (flags & VBM_STREAMING)) return VBM_ERR_UNSUPPORTED;
   if (grid->n_blocks == 0) return VBM_OK;
   if (!d_taps) return VBM_ERR_ARG;
   const DeviceGrid g = device_grid(grid, d_blob);
@@ -671,11 +734,18 @@ extern "C" int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int
       hipLaunchKernelGGL((k_taps_box_cached<true>), gd, bd, brick_lds_bytes(cap), st, g, d_taps, cap);
     else if (cached)
       hipLaunchKernelGGL((k_taps_box_cached<false>), gd, bd, brick_lds_bytes(cap), st, g, d_taps, cap);
-    else if (stream_taps) hipLaunchKernelGGL((k_taps<27, false, true>), gd, bd, 0, st, g, d_taps);
-    else hipLaunchKernelGGL((k_taps<27, false, false>), gd, bd, 0, st, g, d_taps);
+    else if (stream_taps) hipLaunchKernelGGL((k_taps<BoxShape, false, true>), gd, bd, 0, st, g, d_taps);
+    else hipLaunchKernelGGL((k_taps<BoxShape, false, false>), gd, bd, 0, st, g, d_taps);
+  } else if (shape == 7) {
+    if (cached && stream_taps) hipLaunchKernelGGL((k_taps<CrossShape, true, true>), gd, bd, 0, st, g, d_taps);
+    else if (cached) hipLaunchKernelGGL((k_taps<CrossShape, true, false>), gd, bd, 0, st, g, d_taps);
+    else if (stream_taps) hipLaunchKernelGGL((k_taps<CrossShape, false, true>), gd, bd, 0, st, g, d_taps);
+    else hipLaunchKernelGGL((k_taps<CrossShape, false, false>), gd, bd, 0, st, g, d_taps);
   } else {
-    if (cached) hipLaunchKernelGGL((k_taps<7, true, false>), gd, bd, 0, st, g, d_taps);
-    else hipLaunchKernelGGL((k_taps<7, false, false>), gd, bd, 0, st, g, d_taps);
+    if (cached && stream_taps) hipLaunchKernelGGL((k_taps<AxisShape, true, true>), gd, bd, 0, st, g, d_taps);
+    else if (cached) hipLaunchKernelGGL((k_taps<AxisShape, true, false>), gd, bd, 0, st, g, d_taps);
+    else if (stream_taps) hipLaunchKernelGGL((k_taps<AxisShape, false, true>), gd, bd, 0, st, g, d_taps);
+    else hipLaunchKernelGGL((k_taps<AxisShape, false, false>), gd, bd, 0, st, g, d_taps);
   }
   return launch_status();
 }
@@ -701,24 +771,49 @@ extern "C" int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const fl
   return launch_status();
 }
 
+// The 7-direction filters (cross, 19-tap axis): flags pick the resolver and
+// the delivery; LAP only for the cross.
+template <class S, bool LAP>
+void launch_stencil(const DeviceGrid& g, const float* sc, float* out, int C, bool cached, bool streaming,
+                    hipStream_t st) {
+  if (cached && streaming) launch_channels<StencilLauncher<S, true, LAP, true>>(g, sc, out, C, st);
+  else if (cached) launch_channels<StencilLauncher<S, true, LAP, false>>(g, sc, out, C, st);
+  else if (streaming) launch_channels<StencilLauncher<S, false, LAP, true>>(g, sc, out, C, st);
+  else launch_channels<StencilLauncher<S, false, LAP, false>>(g, sc, out, C, st);
+}
+
 extern "C" int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                                 int flags, void* stream) {
   int rc = check_grid(grid, d_blob);
   if (rc) return rc;
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
-  if (flags & VBM_STREAMING) return VBM_ERR_UNSUPPORTED;
-  if (flags & ~(VBM_CACHED | VBM_OP_LAPLACIAN)) return VBM_ERR_ARG;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_OP_LAPLACIAN)) return VBM_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
     hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
     return launch_status();
   }
   const DeviceGrid g = device_grid(grid, d_blob);
-  const bool cached = flags & VBM_CACHED, lap = flags & VBM_OP_LAPLACIAN;
-  if (cached && lap) launch_channels<CrossLauncher<true, true>>(g, d_sidecar, d_out, C, st);
-  else if (cached) launch_channels<CrossLauncher<true, false>>(g, d_sidecar, d_out, C, st);
-  else if (lap) launch_channels<CrossLauncher<false, true>>(g, d_sidecar, d_out, C, st);
-  else launch_channels<CrossLauncher<false, false>>(g, d_sidecar, d_out, C, st);
+  const bool cached = flags & VBM_CACHED, streaming = flags & VBM_STREAMING;
+  if (flags & VBM_OP_LAPLACIAN) launch_stencil<CrossShape, true>(g, d_sidecar, d_out, C, cached, streaming, st);
+  else launch_stencil<CrossShape, false>(g, d_sidecar, d_out, C, cached, streaming, st);
+  return launch_status();
+}
+
+extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                               int flags, void* stream) {
+  int rc = check_grid(grid, d_blob);
+  if (rc) return rc;
+  rc = check_float_buffers(grid, d_sidecar, d_out, C);
+  if (rc) return rc;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (grid->n_blocks == 0) {
+    hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
+    return launch_status();
+  }
+  const DeviceGrid g = device_grid(grid, d_blob);
+  launch_stencil<AxisShape, false>(g, d_sidecar, d_out, C, flags & VBM_CACHED, flags & VBM_STREAMING, st);
   return launch_status();
 }

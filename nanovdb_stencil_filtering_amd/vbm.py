@@ -6,9 +6,11 @@ stream.  The names mirror the C entry points:
 
     build(coords, log2_width)          vbm_build  (host) + copy of the blob to the GPU
     decode(grid)                       vbm_decode
+    decode_sweep(grid)                 vbm_decode_sweep
     stencil_indices(grid, shape, ...)  vbm_stencil_indices
     box_filter(grid, sidecar, ...)     vbm_box_filter
     cross_filter(grid, sidecar, ...)   vbm_cross_filter
+    axis_filter(grid, sidecar, ...)    vbm_axis_filter
 
 There is no CPU fallback: if the library is not built, loading raises.
 """
@@ -32,8 +34,8 @@ GRID_MAGIC = 0x314D4256
 STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN", -4: "VBM_ERR_ALIAS",
           -5: "VBM_ERR_RANGE", -6: "VBM_ERR_HIP", -7: "VBM_ERR_UNSUPPORTED", -8: "VBM_ERR_NOMEM"}
 
-EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_decode", "vbm_stencil_indices", "vbm_box_filter",
-            "vbm_cross_filter", "vbm_strerror")
+EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
+            "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_strerror")
 
 
 class VbmError(RuntimeError):
@@ -74,12 +76,16 @@ def load_library():
     lib.vbm_free_blob.argtypes = [P]
     lib.vbm_decode.restype = I
     lib.vbm_decode.argtypes = [GP, P, P, P, P]
+    lib.vbm_decode_sweep.restype = I
+    lib.vbm_decode_sweep.argtypes = [GP, P, P, P, P]
     lib.vbm_stencil_indices.restype = I
     lib.vbm_stencil_indices.argtypes = [GP, P, I, I, P, P]
     lib.vbm_box_filter.restype = I
     lib.vbm_box_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_cross_filter.restype = I
     lib.vbm_cross_filter.argtypes = [GP, P, P, P, I, I, P]
+    lib.vbm_axis_filter.restype = I
+    lib.vbm_axis_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_strerror.restype = ctypes.c_char_p
     lib.vbm_strerror.argtypes = [I]
     _lib = lib
@@ -195,16 +201,22 @@ def _blob_ptr(grid: Grid):
     return _ptr(grid.blob)
 
 
-def decode(grid: Grid, stream=None):
-    """vbm_decode -> (leafIndex as int32 tensor, voxelOffset as int16 tensor), n_blocks*W each
-    (bit patterns of u32 / u16)."""
+def decode(grid: Grid, stream=None, sweep: bool = False):
+    """vbm_decode (or vbm_decode_sweep) -> (leafIndex as int32 tensor, voxelOffset as int16 tensor),
+    n_blocks*W each (bit patterns of u32 / u16)."""
     import torch
     dev = grid.blob.device
     leaf = torch.empty(grid.n_slots, dtype=torch.int32, device=dev)
     off = torch.empty(grid.n_slots, dtype=torch.int16, device=dev)
-    _check(load_library().vbm_decode(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(leaf), _ptr(off),
-                                     _stream_ptr(stream)), "vbm_decode")
+    lib = load_library()
+    fn, name = (lib.vbm_decode_sweep, "vbm_decode_sweep") if sweep else (lib.vbm_decode, "vbm_decode")
+    _check(fn(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(leaf), _ptr(off), _stream_ptr(stream)), name)
     return leaf, off
+
+
+def decode_sweep(grid: Grid, stream=None):
+    """vbm_decode_sweep: the same maps as decode(), by the sweep the select-based decode replaced."""
+    return decode(grid, stream, sweep=True)
 
 
 def stencil_indices(grid: Grid, shape: int, flags: int = 0, stream=None):
@@ -243,4 +255,12 @@ def cross_filter(grid: Grid, sidecar, flags: int = CACHED | OP_SUM, out=None, st
     _check(load_library().vbm_cross_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
                                            int(sidecar.shape[1]), int(flags), _stream_ptr(stream)),
            "vbm_cross_filter")
+    return out
+
+
+def axis_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, stream=None):
+    """vbm_axis_filter (19-tap axis stencil sum) -> out float32 [(N+1), C]."""
+    out = _filter_out(grid, sidecar, out)
+    _check(load_library().vbm_axis_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
+                                          int(sidecar.shape[1]), int(flags), _stream_ptr(stream)), "vbm_axis_filter")
     return out

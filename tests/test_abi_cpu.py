@@ -98,15 +98,21 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
     assert lib.vbm_decode(h, None, FAKE_DEV, FAKE_DEV, None) == ARG
     assert lib.vbm_decode(h, FAKE_DEV, None, FAKE_DEV, None) == ARG
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 27, 0, None, None) == ARG
+    assert lib.vbm_decode_sweep(None, FAKE_DEV, FAKE_DEV, FAKE_DEV, None) == ARG
+    assert lib.vbm_decode_sweep(h, FAKE_DEV, FAKE_DEV, None, None) == ARG
     # shapes and flags
-    assert lib.vbm_stencil_indices(h, FAKE_DEV, 19, 0, FAKE_DEV, None) == ARG
+    for shape in (0, 8, 18, 26, 28):
+        assert lib.vbm_stencil_indices(h, FAKE_DEV, shape, 0, FAKE_DEV, None) == ARG
+    assert lib.vbm_stencil_indices(h, FAKE_DEV, 19, 0, None, None) == ARG
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 27, 0x40, FAKE_DEV, None) == ARG
-    assert lib.vbm_stencil_indices(h, FAKE_DEV, 7, vbm.STREAMING, FAKE_DEV, None) == UNSUP
+    assert lib.vbm_stencil_indices(h, FAKE_DEV, 7, vbm.OP_LAPLACIAN, FAKE_DEV, None) == ARG
     assert lib.vbm_box_filter(h, FAKE_DEV, sc, out_far, 1, 0x8, None) == ARG
-    assert lib.vbm_cross_filter(h, FAKE_DEV, sc, out_far, 1, vbm.STREAMING, None) == UNSUP
+    assert lib.vbm_box_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
     assert lib.vbm_cross_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
+    assert lib.vbm_axis_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
+    assert lib.vbm_axis_filter(ctypes.byref(bad), FAKE_DEV, sc, out_far, 1, 0, None) == ARG
     # channels, alignment, aliasing
-    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter):
+    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter):
         assert fn(h, FAKE_DEV, sc, out_far, 0, 0, None) == ARG
         assert fn(h, FAKE_DEV, None, out_far, 1, 0, None) == ARG
         assert fn(h, FAKE_DEV, sc, None, 1, 0, None) == ARG

@@ -43,7 +43,7 @@ def test_no_variable_count_64bit_vector_shifts(device_asm):
 
 def test_kernels_present(device_asm):
     names = [n for n, _ in kernels(device_asm)]
-    for k in ("k_decode", "k_taps", "k_box", "k_cross"):
+    for k in ("k_decode", "k_decode_sweep", "k_taps", "k_box", "k_stencil"):
         assert any(k in n for n in names), k
 
 

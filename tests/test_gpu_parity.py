@@ -65,11 +65,12 @@ def u32(t):
 def test_decode(name, log2w):
     g, ref = grid_pair(name, log2w)
     say("decode %s W=%d N=%d" % (name, 1 << log2w, g.n_active))
-    leaf, off = vbm.decode(g)
-    torch.cuda.synchronize()
     rl, ro = ref.decode(log2w)
-    assert np.array_equal(leaf.cpu().numpy().view(np.uint32), rl)
-    assert np.array_equal(off.cpu().numpy().view(np.uint16), ro)
+    for sweep in (False, True):
+        leaf, off = vbm.decode(g, sweep=sweep)
+        torch.cuda.synchronize()
+        assert np.array_equal(leaf.cpu().numpy().view(np.uint32), rl), sweep
+        assert np.array_equal(off.cpu().numpy().view(np.uint16), ro), sweep
 
 
 @pytest.mark.parametrize("log2w", [6, 7, 9])
@@ -83,10 +84,15 @@ def test_stencil_indices(name, log2w):
         t = vbm.stencil_indices(g, 27, flags).cpu().numpy().view(np.uint64)
         assert np.array_equal(t[:N], ref_box), flags
         assert np.all(t[N:] == 0)
-    for flags in (0, vbm.CACHED):
+    ref_axis = ref.taps(19)
+    for flags in (0, vbm.STREAMING, vbm.CACHED, vbm.CACHED | vbm.STREAMING):
         say("taps cross %s W=%d flags=%d" % (name, 1 << log2w, flags))
         t = vbm.stencil_indices(g, 7, flags).cpu().numpy().view(np.uint64)
         assert np.array_equal(t[:N], ref_box[:, CROSS_FROM_BOX]), flags
+        assert np.all(t[N:] == 0)
+        say("taps axis %s W=%d flags=%d" % (name, 1 << log2w, flags))
+        t = vbm.stencil_indices(g, 19, flags).cpu().numpy().view(np.uint64)
+        assert np.array_equal(t[:N], ref_axis), flags
         assert np.all(t[N:] == 0)
 
 
@@ -117,11 +123,26 @@ def test_cross_filter(name, C):
         sct = torch.from_numpy(sc).cuda()
         for op, code in (("sum", vbm.OP_SUM), ("laplacian", vbm.OP_LAPLACIAN)):
             want = ref.cross(sc, op).view(np.uint32)
-            for cached in (0, vbm.CACHED):
-                say("cross %s %s W=%d C=%d cached=%d" % (op, name, 1 << log2w, C, cached))
+            for flags in BOX_FLAGS:
+                say("cross %s %s W=%d C=%d flags=%d" % (op, name, 1 << log2w, C, flags))
                 out = torch.full_like(sct, float("nan"))
-                vbm.cross_filter(g, sct, cached | code, out=out)
-                assert np.array_equal(u32(out), want), (log2w, op, cached)
+                vbm.cross_filter(g, sct, flags | code, out=out)
+                assert np.array_equal(u32(out), want), (log2w, op, flags)
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand"])
+def test_axis_filter(name, C):
+    for log2w in (6, 7, 9):
+        g, ref = grid_pair(name, log2w)
+        sc = I.sidecar(300 + C, g.n_active, C)
+        want = ref.axis(sc).view(np.uint32)
+        sct = torch.from_numpy(sc).cuda()
+        for flags in BOX_FLAGS:
+            say("axis %s W=%d C=%d flags=%d" % (name, 1 << log2w, C, flags))
+            out = torch.full_like(sct, float("nan"))
+            vbm.axis_filter(g, sct, flags, out=out)
+            assert np.array_equal(u32(out), want), (log2w, flags)
 
 
 def test_constant_field_interior_is_27():
@@ -148,6 +169,10 @@ def test_empty_grid_writes_row_zero():
     assert torch.all(out == 0)
     out = vbm.cross_filter(g, sc, vbm.OP_LAPLACIAN)
     assert torch.all(out == 0)
+    out = vbm.axis_filter(g, sc)
+    assert torch.all(out == 0)
+    leaf, off = vbm.decode_sweep(g)
+    assert leaf.numel() == 0 and off.numel() == 0
     leaf, off = vbm.decode(g)
     assert leaf.numel() == 0 and off.numel() == 0
 
@@ -159,6 +184,8 @@ def test_single_voxel():
     assert out.tolist() == [[0.0, 0.0], [1.5, -2.0]]
     lap = vbm.cross_filter(g, sc, vbm.CACHED | vbm.OP_LAPLACIAN).cpu().numpy()
     assert lap.tolist() == [[0.0, 0.0], [-9.0, 12.0]]
+    ax = vbm.axis_filter(g, sc).cpu().numpy()
+    assert ax.tolist() == [[0.0, 0.0], [1.5, -2.0]]
     leaf, off = vbm.decode(g)
     l = leaf.cpu().numpy().view(np.uint32)
     o = off.cpu().numpy().view(np.uint16)
