@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="profile mode: run only this variant (e.g. box_cs) and exit")
+    ap.add_argument("--band", action="store_true",
+                    help="also time the cached streaming box filter on the ~27M-voxel noisy narrow band "
+                         "(W512, C=16; about a minute of set-up)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="profile mode: time a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -230,6 +233,29 @@ def main():
                 rec("%s_W%d" % (nm, gw.width), t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
 
     traffic = counted_traffic() if (C == 16 and W == 128) else None
+
+    if args.band:
+        # configuration 5: noisy narrow band, W512, C=16 (a measurement, not the headline)
+        del scs, outs
+        log("bench: generating the narrow band")
+        band = inputs.band_coords(5, **inputs.BAND)
+        gb = vbm.build(band, 9, device=dev)
+        Nb = gb.n_active
+        log("bench: band N=%d leaves=%d blocks=%d" % (Nb, gb.n_leaves, gb.n_blocks))
+        scb = torch.empty((Nb + 1, 16), dtype=torch.float32, device=dev)
+        step = 1 << 22
+        for a in range(0, Nb + 1, step):
+            b = min(Nb + 1, a + step)
+            scb[a:b] = torch.from_numpy(inputs.sidecar_rows(6, a, b, 16)).to(dev)
+        outb = torch.empty_like(scb)
+        tb = time_launches(lambda k: vbm.box_filter(gb, scb, flags_cs, out=outb), 1, 10, 3)
+        abb = alg_bytes_filter(Nb, gb.n_leaves, gb.n_blocks, gb.width, 16)
+        extra["band_box_cached_streaming_W512_C16"] = {
+            "ms": round(tb, 4), "GBps": round(abb / (tb * 1e-3) / 1e9, 1),
+            "hbm_frac": round(abb / (tb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "voxel_ch_per_s": float("%.4e" % (Nb * 16 / (tb * 1e-3))), "n_active": Nb}
+        log("  band box cached streaming W512 C16: %.4f ms, %.1f GB/s" % (tb, abb / (tb * 1e-3) / 1e9))
+        del scb, outb, gb
 
     cpu = None
     if not args.no_cpu:

@@ -74,6 +74,16 @@ def sidecar(seed: int, n_active: int, channels: int) -> np.ndarray:
     return v
 
 
+def sidecar_rows(seed: int, row0: int, row1: int, channels: int) -> np.ndarray:
+    """Rows row0 .. row1-1 of ``sidecar(seed, n, channels)`` (same values), so a
+    large sidecar can be produced a slice at a time."""
+    k = np.arange(row0 * channels, row1 * channels, dtype=np.uint64)
+    v = _uniform_pm1_f32(splitmix64(seed, k)).reshape(row1 - row0, channels)
+    if row0 == 0:
+        v[0, :] = 0.0
+    return v
+
+
 def shell_coords(radius: float, half_thickness: float) -> np.ndarray:
     """All integer points p with | ||p|| - radius | <= half_thickness, centred on the origin.
 

@@ -81,3 +81,18 @@ def test_build_is_order_and_duplicate_invariant():
     h1, b1 = vbm.build_host(c, 8)
     h2, b2 = vbm.build_host(np.concatenate([I.shuffled(c, 3), c[::7]]), 8)
     assert bytes(h1) == bytes(h2) and np.array_equal(b1, b2)
+
+
+def test_sidecar_rows_slices_the_sidecar():
+    full = I.sidecar(7, 3000, 3)
+    parts = [I.sidecar_rows(7, a, min(3001, a + 700), 3) for a in range(0, 3001, 700)]
+    assert np.array_equal(np.concatenate(parts), full)
+
+
+def test_tabulated_noise_equals_value_noise():
+    """The narrow-band generator's tabulated lattice noise gives the same float64
+    values as the direct value noise."""
+    rng = np.random.default_rng(3)
+    p = rng.uniform(-300.0, 300.0, size=(2000, 3))
+    tab = I._LatticeNoise(5, -301, 301, total_amplitude=20.0)
+    assert np.array_equal(tab(p), I.value_noise(5, p, total_amplitude=20.0))
