@@ -216,6 +216,11 @@ def main():
         # hot-cache figure (single buffer set; the Infinity Cache may serve it)
         t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
         rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
+        # device-side metadata build (leaf directories, leafFirst, block metadata)
+        for w in (7, 9):
+            gw = grids[w]
+            t = time_launches(lambda k: vbm.build_metadata(gw), 1, 20, 5)
+            rec("build_metadata_W%d" % gw.width, t, 2 * 80 * L + (4 + gw.width // 8) * gw.n_blocks)
         # decode: select-based vs the sweep it replaced, every width (the pages' A/B)
         lib = vbm.load_library()
         import ctypes

@@ -127,6 +127,26 @@ int vbm_build(const int32_t* ijk, int64_t n, int log2_width, vbm_grid* grid, voi
 void vbm_free_blob(void* host_blob);
 
 /*
+ * Device-side VBM metadata build: from the leaf masks in d_blob, recompute on
+ * the GPU every field the index grid and the VBM derive from them (openvdb PR
+ * #2258, "What changed": the 9-bit prefix-sum directory; openvdb PR #2263,
+ * "Built on the register-decode API": firstLeafID and the jumpMap of each
+ * block):
+ *   leaf prefix   field k = active voxels in mask words 0..k
+ *   leaf first    1 + active voxels in all earlier leaves (tree order)
+ *   block_first_leaf, block_jump   as vbm_build writes them
+ * For a blob from vbm_build the result equals the host's bytes.  A caller may
+ * edit leaf masks in place on the device and rebuild with this call as long as
+ * every leaf keeps at least one active voxel and the total stays n_active (the
+ * block sections are sized by it); the new total is written to *d_total (a
+ * device u64; NULL to skip) so the caller can check.  The tree sections (root,
+ * upper, lower) and the leaf origins are read-only here.  Asynchronous on
+ * `stream`; the blob must not be in use by other work on other streams.
+ * Errors: VBM_ERR_ARG, VBM_ERR_HIP.
+ */
+int vbm_build_metadata(const vbm_grid* grid, void* d_blob, uint64_t* d_total, void* stream);
+
+/*
  * Inverse-map decode of every slot (openvdb PR #2258, "What changed": rank of
  * the slot into the block's jumpMap picks the leaf; the prefix directory picks
  * the 64-bit mask word; an in-word select recovers the voxel offset).

@@ -550,6 +550,104 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
   store_row<CH, VEC>(out + idx * C + ch0, acc);
 }
 
+// ---------------------------------------------------------------------------
+// device-side VBM metadata build
+// ---------------------------------------------------------------------------
+//
+// From the leaf masks in the blob, the device recomputes what the index grid
+// and the VBM derive from them (openvdb PR #2258, "What changed"; openvdb PR
+// #2263, "Built on the register-decode API"):
+//   * per leaf the 9-bit prefix directory (field k = active voxels in mask
+//     words 0..k) and leafFirst (1 + active voxels in all earlier leaves);
+//   * per block the leaf owning its first index and the jumpMap bits of the
+//     slots >= 1 whose index starts a leaf.
+// Three launches: per-leaf counts and directories, one workgroup scanning the
+// counts in place into leafFirst, one wave per block for its metadata.
+
+struct MutableGrid {
+  Leaf* leaves;
+  uint32_t* block_first_leaf;
+  uint64_t* block_jump;
+  uint32_t n_leaves;
+  uint32_t n_blocks;
+  int32_t log2w;
+};
+
+// Per leaf: prefix directory, and the active count parked in `first` for the scan.
+__global__ void __launch_bounds__(256) k_meta_counts(MutableGrid m) {
+  const uint32_t l = blockIdx.x * blockDim.x + threadIdx.x;
+  if (l >= m.n_leaves) return;
+  Leaf& L = m.leaves[l];
+  uint32_t count = 0, lo = 0, hi = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < 8; ++w) {
+    count += __popcll(L.mask[w]);
+    if (w < 7) {  // field w at bits 9w .. 9w+8, assembled in two 32-bit halves
+      const uint32_t p = 9 * w;
+      if (p < 32) lo |= count << p;
+      if (p + 9 > 32) hi |= p < 32 ? count >> (32 - p) : count << (p - 32);
+    }
+  }
+  L.prefix = uint64_t(lo) | (uint64_t(hi) << 32);
+  L.first = count;
+}
+
+// One workgroup: leaf l's count becomes leafFirst = 1 + sum of the counts of
+// leaves 0..l-1.  Each work-item owns a contiguous run of leaves.
+__global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint64_t* __restrict__ total) {
+  __shared__ uint64_t part[1024];
+  const uint32_t T = blockDim.x, t = threadIdx.x;
+  const uint32_t per = (m.n_leaves + T - 1) / T;
+  const uint32_t a = min(m.n_leaves, t * per), e = min(m.n_leaves, a + per);
+  uint64_t s = 0;
+  for (uint32_t l = a; l < e; ++l) s += m.leaves[l].first;
+  part[t] = s;
+  __syncthreads();
+  for (uint32_t d = 1; d < T; d <<= 1) {  // inclusive scan of the runs' sums
+    const uint64_t v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  uint64_t run = 1 + (t ? part[t - 1] : 0);
+  for (uint32_t l = a; l < e; ++l) {
+    const uint64_t c = m.leaves[l].first;
+    m.leaves[l].first = run;
+    run += c;
+  }
+  if (t == T - 1 && total) *total = part[T - 1];
+}
+
+// One wave per block: the leaf owning index g0 = 1 + bW (binary search over
+// leafFirst), then the leaves starting inside the block set their jumpMap bits.
+__global__ void __launch_bounds__(64) k_meta_blocks(MutableGrid m) {
+  __shared__ uint32_t words[16];  // the block's jumpMap as 32-bit halves
+  const uint32_t b = blockIdx.x, lane = threadIdx.x;
+  const uint32_t W = 1u << m.log2w;
+  const uint64_t g0 = 1 + (uint64_t(b) << m.log2w);
+  if (lane < 2 * (W / 64)) words[lane] = 0;
+  uint32_t lo = 0, hi = m.n_leaves;  // first leaf with leafFirst > g0
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (m.leaves[mid].first <= g0) lo = mid + 1; else hi = mid;
+  }
+  const uint32_t first = lo - 1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (uint32_t l = first + 1 + lane; l < m.n_leaves; l += 64) {
+    const uint64_t s = m.leaves[l].first - g0;
+    if (s >= W) break;  // leafFirst grows with l: later leaves start past the block
+    __hip_atomic_fetch_or(&words[s >> 5], 1u << (s & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane == 0) m.block_first_leaf[b] = first;
+  if (lane < W / 64)
+    m.block_jump[uint64_t(b) * (W / 64) + lane] = uint64_t(words[2 * lane]) | (uint64_t(words[2 * lane + 1]) << 32);
+}
+
 __global__ void k_zero_index_row(float* __restrict__ out, uint32_t C) {
   for (uint32_t c = threadIdx.x; c < C; c += blockDim.x) out[c] = 0.0f;
 }
@@ -815,5 +913,24 @@ extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const f
   }
   const DeviceGrid g = device_grid(grid, d_blob);
   launch_stencil<AxisShape, false>(g, d_sidecar, d_out, C, flags & VBM_CACHED, flags & VBM_STREAMING, st);
+  return launch_status();
+}
+
+extern "C" int vbm_build_metadata(const vbm_grid* grid, void* d_blob, uint64_t* d_total, void* stream) {
+  int rc = check_grid(grid, d_blob);
+  if (rc) return rc;
+  if (grid->n_leaves == 0) return VBM_OK;
+  uint8_t* base = static_cast<uint8_t*>(d_blob);
+  MutableGrid m;
+  m.leaves = reinterpret_cast<Leaf*>(base + grid->off_leaves);
+  m.block_first_leaf = reinterpret_cast<uint32_t*>(base + grid->off_block_first_leaf);
+  m.block_jump = reinterpret_cast<uint64_t*>(base + grid->off_block_jump);
+  m.n_leaves = grid->n_leaves;
+  m.n_blocks = grid->n_blocks;
+  m.log2w = grid->log2_width;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_meta_counts, dim3((m.n_leaves + 255) / 256), dim3(256), 0, st, m);
+  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(1024), 0, st, m, d_total);
+  if (m.n_blocks) hipLaunchKernelGGL(k_meta_blocks, dim3(m.n_blocks), dim3(64), 0, st, m);
   return launch_status();
 }

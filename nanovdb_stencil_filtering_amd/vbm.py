@@ -5,6 +5,7 @@ kernels behind the C ABI.  PyTorch provides device memory and the current
 stream.  The names mirror the C entry points:
 
     build(coords, log2_width)          vbm_build  (host) + copy of the blob to the GPU
+    build_metadata(grid)               vbm_build_metadata (device-side leaf/block metadata)
     decode(grid)                       vbm_decode
     decode_sweep(grid)                 vbm_decode_sweep
     stencil_indices(grid, shape, ...)  vbm_stencil_indices
@@ -34,7 +35,7 @@ GRID_MAGIC = 0x314D4256
 STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN", -4: "VBM_ERR_ALIAS",
           -5: "VBM_ERR_RANGE", -6: "VBM_ERR_HIP", -7: "VBM_ERR_UNSUPPORTED", -8: "VBM_ERR_NOMEM"}
 
-EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
+EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_build_metadata", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
             "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_strerror")
 
 
@@ -74,6 +75,8 @@ def load_library():
     lib.vbm_build.argtypes = [P, I64, I, GP, ctypes.POINTER(ctypes.c_void_p)]
     lib.vbm_free_blob.restype = None
     lib.vbm_free_blob.argtypes = [P]
+    lib.vbm_build_metadata.restype = I
+    lib.vbm_build_metadata.argtypes = [GP, P, P, P]
     lib.vbm_decode.restype = I
     lib.vbm_decode.argtypes = [GP, P, P, P, P]
     lib.vbm_decode_sweep.restype = I
@@ -185,6 +188,17 @@ def build(coords: np.ndarray, log2_width: int, device="cuda") -> Grid:
     hdr, host = build_host(coords, log2_width)
     blob = torch.from_numpy(host).to(device)
     return Grid(hdr, blob)
+
+
+def build_metadata(grid: Grid, stream=None):
+    """vbm_build_metadata: recompute the leaf prefix directories and leafFirst and the
+    block metadata of grid.blob on the device from its leaf masks; returns the total
+    active count as a one-element int64 device tensor."""
+    import torch
+    total = torch.zeros(1, dtype=torch.int64, device=grid.blob.device)
+    _check(load_library().vbm_build_metadata(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(total),
+                                             _stream_ptr(stream)), "vbm_build_metadata")
+    return total
 
 
 def _stream_ptr(stream):

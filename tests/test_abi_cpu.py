@@ -98,6 +98,8 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
     assert lib.vbm_decode(h, None, FAKE_DEV, FAKE_DEV, None) == ARG
     assert lib.vbm_decode(h, FAKE_DEV, None, FAKE_DEV, None) == ARG
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 27, 0, None, None) == ARG
+    assert lib.vbm_build_metadata(None, FAKE_DEV, None, None) == ARG
+    assert lib.vbm_build_metadata(h, None, None, None) == ARG
     assert lib.vbm_decode_sweep(None, FAKE_DEV, FAKE_DEV, FAKE_DEV, None) == ARG
     assert lib.vbm_decode_sweep(h, FAKE_DEV, FAKE_DEV, None, None) == ARG
     # shapes and flags

@@ -190,3 +190,80 @@ def test_single_voxel():
     l = leaf.cpu().numpy().view(np.uint32)
     o = off.cpu().numpy().view(np.uint16)
     assert l[0] == 0 and o[0] == (3 * 64 + 0 * 8 + 3) and np.all(l[1:] == 0xFFFFFFFF) and np.all(o[1:] == 0xFFFF)
+
+
+def _scribble_metadata(g):
+    """Overwrite, on the device, every field vbm_build_metadata recomputes."""
+    h = g.hdr
+    L, nb, W = h.n_leaves, h.n_blocks, 1 << h.log2_width
+    leaves = g.blob[h.off_leaves:h.off_leaves + L * 128].view(L, 128)
+    leaves[:, 64:80] = 0xA5                                   # prefix directory and leafFirst
+    g.blob[h.off_block_first_leaf:h.off_block_first_leaf + nb * 4] = 0x5A
+    g.blob[h.off_block_jump:h.off_block_jump + nb * W // 8] = 0xC3
+
+
+@pytest.mark.parametrize("log2w", [6, 7, 9])
+@pytest.mark.parametrize("name", sorted(GRIDS))
+def test_build_metadata_equals_host(name, log2w):
+    coords = GRIDS[name]()
+    hdr, host = vbm.build_host(coords, log2w)
+    g = vbm.Grid(hdr, torch.from_numpy(host.copy()).cuda())
+    _scribble_metadata(g)
+    say("build_metadata %s W=%d" % (name, 1 << log2w))
+    total = vbm.build_metadata(g)
+    assert int(total.item()) == hdr.n_active
+    assert np.array_equal(g.blob.cpu().numpy(), host)
+
+
+def test_build_metadata_after_in_place_edit():
+    """Move one voxel inside each of a set of leaves (clear a set bit, set a clear
+    one) directly in the device masks, rebuild the metadata on the device, and
+    check the rebuilt grid against the oracle built from the edited coordinates:
+    leaf directories and leafFirst, block metadata, decode, box filter."""
+    coords = I.random_sparse_coords(8, (40, 40, 40), 0.3, (-20, 3, 100))
+    for log2w in (6, 7, 9):
+        hdr, host = vbm.build_host(coords, log2w)
+        sec = vbm.blob_sections(hdr, host)
+        lv = sec["leaves"]
+        rng = np.random.default_rng(log2w)
+        masks = lv["mask"].copy()
+        moved_from, moved_to = [], []
+        for l in rng.choice(hdr.n_leaves, size=hdr.n_leaves // 3, replace=False):
+            bits = np.unpackbits(masks[l].view(np.uint8), bitorder="little")
+            on, off = np.nonzero(bits)[0], np.nonzero(bits == 0)[0]
+            if on.size == 0 or off.size == 0:
+                continue
+            a, b = int(rng.choice(on)), int(rng.choice(off))
+            masks[l, a // 64] &= ~np.uint64(1 << (a % 64))
+            masks[l, b // 64] |= np.uint64(1 << (b % 64))
+            o = lv["origin"][l].astype(np.int64)
+            moved_from.append(o + [a >> 6, (a >> 3) & 7, a & 7])
+            moved_to.append(o + [b >> 6, (b >> 3) & 7, b & 7])
+        assert moved_from
+        gone = {tuple(p) for p in moved_from}
+        new_coords = np.array([p for p in map(tuple, coords.tolist()) if p not in gone] +
+                              [tuple(p) for p in moved_to], np.int32)
+        ref = oracle.OracleGrid(new_coords)
+        assert ref.n_active == hdr.n_active and ref.n_leaves == hdr.n_leaves
+        g = vbm.Grid(hdr, torch.from_numpy(host.copy()).cuda())
+        L = hdr.n_leaves
+        g.blob[hdr.off_leaves:hdr.off_leaves + L * 128].view(L, 128)[:, 0:64] = \
+            torch.from_numpy(masks.view(np.uint8).reshape(L, 64)).cuda()
+        say("build_metadata after edit W=%d, %d voxels moved" % (1 << log2w, len(moved_from)))
+        total = vbm.build_metadata(g)
+        assert int(total.item()) == hdr.n_active
+        got = vbm.blob_sections(hdr, g.blob.cpu().numpy())
+        rl = ref.leaves()
+        assert np.array_equal(got["leaves"]["mask"], rl["mask"])
+        assert np.array_equal(got["leaves"]["prefix"], rl["prefix"])
+        assert np.array_equal(got["leaves"]["first"], rl["first"])
+        rb = ref.blocks(log2w)
+        assert np.array_equal(got["block_first_leaf"], rb["first_leaf"])
+        assert np.array_equal(got["block_jump"], rb["jump"])
+        leaf, off = vbm.decode(g)
+        dl, do = ref.decode(log2w)
+        assert np.array_equal(leaf.cpu().numpy().view(np.uint32), dl)
+        assert np.array_equal(off.cpu().numpy().view(np.uint16), do)
+        sc = I.sidecar(77, hdr.n_active, 4)
+        out = vbm.box_filter(g, torch.from_numpy(sc).cuda(), vbm.CACHED | vbm.STREAMING)
+        assert np.array_equal(u32(out), ref.box(sc).view(np.uint32))
