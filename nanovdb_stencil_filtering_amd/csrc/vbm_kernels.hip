@@ -160,6 +160,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_XCD_REMAP
 #define VBM_XCD_REMAP 1    // 1: give each of the 8 XCDs a contiguous range of blocks
 #endif
+#ifndef VBM_NT_STORE
+#define VBM_NT_STORE 1  // 1: output rows written with non-temporal stores
+#endif
 #ifndef VBM_SPLIT_MAX
 #define VBM_SPLIT_MAX 256  // work-items per workgroup of the split-row kernel (at least W)
 #endif
@@ -431,7 +434,12 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       return o == kInactive ? o : o + 16 * q;
     });
     const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + slot;
+#if VBM_NT_STORE
+    f32x4* dst = reinterpret_cast<f32x4*>(out + idx * C + ch0) + q;
+    __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, dst);
+#else
     reinterpret_cast<float4*>(out + idx * C + ch0)[q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#endif
   };
   // Phase 1: the waves holding slots decode them (lane-rank decode; a slot
   // past the last index is marked 0xFFFFFFFF) while the other waves stage the

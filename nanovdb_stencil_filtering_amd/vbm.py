@@ -68,6 +68,10 @@ def load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libvbm.so is not built (%s); run __graft_entry__.build() or "
                           "python -m nanovdb_stencil_filtering_amd.build" % LIB_PATH)
+    # torch brings its own HIP runtime; loading it first makes libvbm.so bind to
+    # that same runtime, so torch's device pointers and streams are valid in the
+    # library's launches (a second runtime would reject torch's stream handles).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     GP = ctypes.POINTER(GridHeader)
