@@ -404,9 +404,10 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
 // LANES = CH / 4 work-items (one float4 of channels each): a wave gathers
 // 64 / LANES whole rows per load instead of one 16-byte piece of 64 rows, and
 // writes whole output rows.  Slots are decoded once into LDS; the workgroup
-// has min(W * LANES, 1024) work-items, each handling W * LANES / blockDim
-// (slot, quarter) tasks.  Taps are streamed from the brick in tap order.
-template <int CH>
+// has min(W * LANES, max(W, VBM_SPLIT_MAX)) work-items, each handling one or
+// more (slot, quarter) tasks.  STREAM: taps are streamed from the brick in tap
+// order; else the 27 taps are materialised into an array first.
+template <int CH, bool STREAM>
 __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const float* __restrict__ sc,
                                                            uint32_t sc_bytes, float* __restrict__ out, uint32_t C,
                                                            uint32_t ch0, uint32_t cap) {
@@ -483,7 +484,14 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       const uint32_t j = info >> 16;
       if (info == 0xFFFFFFFFu || j - j0 >= count) continue;
       const uint32_t* corner = brick + (j - j0) * kBrickCells + (info & 0xFFFF);
-      run(task, [&](int t) { return corner[box_brick_offset(t)]; });
+      if constexpr (STREAM) {
+        run(task, [&](int t) { return corner[box_brick_offset(t)]; });
+      } else {  // the 27 taps materialised into an array first
+        uint32_t st[kBoxTaps];
+#pragma unroll
+        for (int t = 0; t < kBoxTaps; ++t) st[t] = corner[box_brick_offset(t)];
+        run(task, [&](int t) { return st[t]; });
+      }
     }
   }
 }
@@ -729,12 +737,12 @@ struct BoxLauncher {
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
-    if constexpr (CACHED && VEC && STREAM && (CH == 8 || CH == 16)) {
+    if constexpr (CACHED && VEC && (CH == 8 || CH == 16)) {
       const uint32_t cap = brick_capacity(g.log2w);
       const uint32_t W = 1u << g.log2w;
       const uint32_t tasks = W * (CH / 4);
       const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
-      hipLaunchKernelGGL((k_box_cached_split<CH>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
+      hipLaunchKernelGGL((k_box_cached_split<CH, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
                          brick_lds_bytes(cap) + W * 4, st, g, sc, bytes, out, C, ch0, cap);
     } else if constexpr (CACHED) {
       const uint32_t cap = brick_capacity(g.log2w);
