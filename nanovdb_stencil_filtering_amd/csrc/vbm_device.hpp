@@ -384,14 +384,79 @@ __device__ __forceinline__ ColumnBits column_bits(const DeviceGrid& g, uint32_t 
   return ColumnBits{ok ? bits : 0u, uint32_t(L.first) + before + below};
 }
 
+// The first 80 bytes of a leaf record (mask words, prefix directory, first
+// index) copied to LDS as five 16-byte pieces; zeros for an absent leaf.
+struct StagedLeaf {
+  uint64_t mask[8];
+  uint64_t prefix;
+  uint64_t first;
+};
+static_assert(sizeof(StagedLeaf) == 80, "staged leaf is five 16-byte pieces");
+
+// column_bits on a staged leaf record (an absent leaf has an empty mask).
+__device__ __forceinline__ ColumnBits column_bits_staged(const StagedLeaf& L, uint32_t wx, uint32_t y8) {
+  const uint64_t m = L.mask[wx];
+  const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+  const bool upper = y8 >= 32;
+  const uint32_t half = upper ? hi : lo;
+  const uint32_t sh = y8 & 31;
+  const uint32_t below = __popc(__builtin_amdgcn_ubfe(half, 0, sh)) + (upper ? __popc(lo) : 0u);
+  const uint32_t before = wx ? prefix_field(L.prefix, wx - 1) : 0u;
+  return ColumnBits{__builtin_amdgcn_ubfe(half, sh, 8), uint32_t(L.first) + before + below};
+}
+
+// x range of the block's voxels in each spanned leaf, for the brick build.
+// The block's slots of one leaf are consecutive and, in tree order, ascend in
+// x, so the leaf's first slot in the block holds its lowest x and its last
+// slot its highest.  The work-item of slot s = threadIdx.x (s < W) records
+// them: xr[j] = lowest x and xr[kMaxCachedLeaves + j] = highest x of spanned
+// leaf j < kMaxCachedLeaves.  A slot starts its leaf's run when s = 0 or its
+// jumpMap bit is set, and ends it when s = W - 1, it holds the grid's last
+// index, or bit s + 1 is set.  No barrier.
+__device__ __forceinline__ void record_leaf_xrange(const DeviceGrid& g, uint32_t b, const Slot& s, uint32_t first,
+                                                   uint32_t* xr) {
+  if (s.leaf == kSentinelLeaf) return;
+  const uint32_t j = s.leaf - first;
+  if (j >= uint32_t(kMaxCachedLeaves)) return;
+  const uint32_t slot = threadIdx.x, lane = slot & 63;
+  const uint32_t words = 1u << (g.log2w - 6);
+  const uint64_t* jm = g.block_jump + uint64_t(b) * words;
+  const uint32_t wi = __builtin_amdgcn_readfirstlane(slot >> 6);  // wave index in the workgroup
+  const uint64_t w = jm[wi];
+  const uint32_t lo = uint32_t(w), hi = uint32_t(w >> 32);
+  const uint32_t next = wi + 1 < words ? uint32_t(jm[wi + 1]) : 0u;  // bit 0 follows lane 63
+  auto bit = [&](uint32_t k) {  // bit k of the wave's word, k <= 64 (32-bit shifts only)
+    return k < 32 ? (lo >> k) & 1u : k < 64 ? (hi >> (k - 32)) & 1u : next & 1u;
+  };
+  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + slot;
+  const bool starts = slot == 0 || bit(lane);
+  const bool ends = slot + 1 == (1u << g.log2w) || idx == g.n_active || bit(lane + 1);
+  const uint32_t x = s.offset >> 6;
+  if (starts) xr[j] = x;
+  if (ends) xr[kMaxCachedLeaves + j] = x;
+}
+
 // Resolve the bricks of `count` spanned leaves whose neighbour tables are
-// table[jj * 27 + dir], jj < count, into brick[jj * kBrickCells + ...].  All
-// threads of the block; ends with a barrier.
+// table[jj * 27 + dir], jj < count, into brick[jj * kBrickCells + ...].  Only
+// the x planes a voxel of the block can reach are resolved: xr[jj] .. xr[jj +
+// kMaxCachedLeaves] (from record_leaf_xrange) grown by one on each side; the
+// other planes of a brick are left unwritten and are never read.  All threads
+// of the block; ends with a barrier.
 __device__ __forceinline__ void build_bricks(const DeviceGrid& g, const uint32_t* table, uint32_t count,
-                                             uint32_t scale, uint32_t sentinel, uint32_t* brick) {
-  for (uint32_t c = threadIdx.x; c < count * 100; c += blockDim.x) {
-    const uint32_t jj = c / 100, xy = c - jj * 100;
-    const uint32_t xp = xy / 10, yp = xy - xp * 10;
+                                             const uint32_t* xr, uint32_t scale, uint32_t sentinel,
+                                             uint32_t* brick) {
+  uint32_t total = 0;
+  for (uint32_t jj = 0; jj < count; ++jj) total += (xr[kMaxCachedLeaves + jj] - xr[jj] + 3) * 10;
+  for (uint32_t c = threadIdx.x; c < total; c += blockDim.x) {
+    // column c -> (brick jj, plane xp, row yp): bricks in order, each over its planes
+    uint32_t jj = 0, rem = c, xp0 = xr[0];
+    for (;;) {
+      const uint32_t n = (xr[kMaxCachedLeaves + jj] - xp0 + 3) * 10;
+      if (rem < n) break;
+      rem -= n;
+      xp0 = xr[++jj];
+    }
+    const uint32_t xp = xp0 + rem / 10, yp = rem % 10;  // plane xp holds x = xp - 1
     const int x = int(xp) - 1, y = int(yp) - 1;
     const int dxl = x >> 3, dyl = y >> 3;  // -1, 0, +1
     const uint32_t wx = uint32_t(x) & 7, y8 = (uint32_t(y) & 7) << 3;
@@ -407,6 +472,58 @@ __device__ __forceinline__ void build_bricks(const DeviceGrid& g, const uint32_t
     out[9] = (zp.bits & 1u) ? zp.base * scale : sentinel;
   }
   __syncthreads();
+}
+
+// build_bricks over leaf records staged in LDS: staged[jj * 27 + dir] is the
+// record of table entry jj * 27 + dir (see fill_table_range_staged).
+__device__ __forceinline__ void build_bricks_staged(const StagedLeaf* staged, uint32_t count, const uint32_t* xr,
+                                                    uint32_t scale, uint32_t sentinel, uint32_t* brick) {
+  uint32_t total = 0;
+  for (uint32_t jj = 0; jj < count; ++jj) total += (xr[kMaxCachedLeaves + jj] - xr[jj] + 3) * 10;
+  for (uint32_t c = threadIdx.x; c < total; c += blockDim.x) {
+    uint32_t jj = 0, rem = c, xp0 = xr[0];
+    for (;;) {
+      const uint32_t n = (xr[kMaxCachedLeaves + jj] - xp0 + 3) * 10;
+      if (rem < n) break;
+      rem -= n;
+      xp0 = xr[++jj];
+    }
+    const uint32_t xp = xp0 + rem / 10, yp = rem % 10;  // plane xp holds x = xp - 1
+    const int x = int(xp) - 1, y = int(yp) - 1;
+    const int dxl = x >> 3, dyl = y >> 3;  // -1, 0, +1
+    const uint32_t wx = uint32_t(x) & 7, y8 = (uint32_t(y) & 7) << 3;
+    const StagedLeaf* row = staged + jj * 27 + (dxl + 1) * 9 + (dyl + 1) * 3;
+    const ColumnBits zm = column_bits_staged(row[0], wx, y8);  // -z neighbour, its z = 7
+    const ColumnBits zc = column_bits_staged(row[1], wx, y8);  // the leaf column, z = 0..7
+    const ColumnBits zp = column_bits_staged(row[2], wx, y8);  // +z neighbour, its z = 0
+    uint32_t* out = brick + jj * kBrickCells + xp * 100 + yp * 10;
+    out[0] = ((zm.bits >> 7) & 1u) ? (zm.base + __popc(zm.bits & 0x7Fu)) * scale : sentinel;
+#pragma unroll
+    for (uint32_t z = 0; z < 8; ++z)
+      out[1 + z] = ((zc.bits >> z) & 1u) ? (zc.base + __popc(zc.bits & ((1u << z) - 1u))) * scale : sentinel;
+    out[9] = (zp.bits & 1u) ? zp.base * scale : sentinel;
+  }
+  __syncthreads();
+}
+
+// fill_table_range that also copies each entry's leaf record into
+// staged[e] (16-byte aligned LDS), so the brick build reads the masks from
+// LDS instead of gathering them from global memory column by column.
+__device__ __forceinline__ void fill_table_range_staged(const DeviceGrid& g, uint32_t first, uint32_t count,
+                                                        StagedLeaf* staged, uint32_t worker, uint32_t workers) {
+  for (uint32_t e = worker; e < count * 27; e += workers) {
+    const uint32_t j = e / 27, dir = e - j * 27;
+    const int dx = int(dir) / 9 - 1, dy = (int(dir) / 3) % 3 - 1, dz = int(dir) % 3 - 1;
+    const uint32_t leaf = (dx | dy | dz) ? neighbour_leaf(g, g.leaves[first + j], dx, dy, dz) : first + j;
+    const bool ok = leaf != kNoLeaf;
+    const uint4* src = reinterpret_cast<const uint4*>(&g.leaves[ok ? leaf : 0u]);
+    uint4* dst = reinterpret_cast<uint4*>(staged + e);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const uint4 v = src[k];
+      dst[k] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
 }
 
 // Fill the neighbour-leaf table of the `count` spanned leaves starting at

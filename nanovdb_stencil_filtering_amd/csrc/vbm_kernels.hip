@@ -169,6 +169,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_PIPE_SPLIT
 #define VBM_PIPE_SPLIT 8   // taps in flight per work-item in the split-row kernel
 #endif
+#ifndef VBM_STAGE_LEAVES
+#define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
+#endif
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  With VBM_XCD_REMAP the workgroup id is mapped so that XCD k works on
@@ -196,6 +199,13 @@ __host__ __device__ constexpr uint32_t box_grid_size(uint32_t n_blocks) {
 // Dynamic LDS of the brick-cached kernels: the neighbour table of up to `cap`
 // spanned leaves, then their bricks.
 __host__ __device__ constexpr uint32_t brick_lds_bytes(uint32_t cap) { return cap * 27 * 4 + cap * kBrickCells * 4; }
+
+// Dynamic LDS of the split-row kernel: staged leaf records (or the neighbour
+// table), the per-slot brick corners and the bricks.
+__host__ __device__ constexpr uint32_t split_lds_bytes(uint32_t cap, uint32_t W) {
+  return VBM_STAGE_LEAVES ? cap * 27 * uint32_t(sizeof(StagedLeaf)) + W * 4 + cap * kBrickCells * 4
+                          : brick_lds_bytes(cap) + W * 4;
+}
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -246,6 +256,7 @@ __global__ void __launch_bounds__(512) k_decode_sweep(DeviceGrid g, uint32_t* __
 template <bool STREAM>
 __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t* __restrict__ taps, uint32_t cap) {
   extern __shared__ uint32_t lds[];
+  __shared__ uint32_t xr[2 * kMaxCachedLeaves];
   uint32_t* table = lds;
   uint32_t* brick = lds + cap * 27;
   const uint32_t b = blockIdx.x;
@@ -257,12 +268,13 @@ __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t*
   if (span > kMaxCachedLeaves) {
     if (valid) for_each_box(g, s, [&](int t, uint32_t idx) { out[t] = idx; });
   } else {
+    record_leaf_xrange(g, b, s, first, xr);
     const uint32_t j = valid ? s.leaf - first : 0xFFFFFFFFu;
     for (uint32_t j0 = 0; j0 < span; j0 += cap) {
       const uint32_t count = min(cap, span - j0);
       if (j0) __syncthreads();
       stage_table_range(g, first + j0, count, table);
-      build_bricks(g, table, count, 1u, 0u, brick);
+      build_bricks(g, table, count, xr + j0, 1u, 0u, brick);
       if (j - j0 < count) {
         const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
         if constexpr (STREAM) {
@@ -355,6 +367,7 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
                                                     float* __restrict__ out, uint32_t C, uint32_t ch0, uint32_t cap) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
   extern __shared__ uint32_t lds[];
+  __shared__ uint32_t xr[2 * kMaxCachedLeaves];
   uint32_t* table = lds;
   uint32_t* brick = lds + cap * 27;
   const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
@@ -376,12 +389,13 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
       });
     }
   } else {
+    record_leaf_xrange(g, b, s, first, xr);
     const uint32_t j = valid ? s.leaf - first : 0xFFFFFFFFu;
     for (uint32_t j0 = 0; j0 < span; j0 += cap) {
       const uint32_t count = min(cap, span - j0);
       if (j0) __syncthreads();
       stage_table_range(g, first + j0, count, table);
-      build_bricks(g, table, count, side.row_bytes, kInactive, brick);
+      build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
       if (j - j0 < count) {
         const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
         if constexpr (STREAM) {
@@ -414,11 +428,18 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   static_assert(CH % 4 == 0 && CH >= 8, "split rows need whole float4 groups");
   constexpr uint32_t LANES = CH / 4;
   constexpr int kPipe = VBM_PIPE_SPLIT;
-  extern __shared__ uint32_t lds[];
+  extern __shared__ uint4 lds4[];
+  __shared__ uint32_t xr[2 * kMaxCachedLeaves];
   const uint32_t W = 1u << g.log2w;
-  uint32_t* slot_corner = lds;             // per slot: brick corner (cell index) | leaf-in-block << 16
-  uint32_t* table = lds + W;
+#if VBM_STAGE_LEAVES
+  StagedLeaf* staged = reinterpret_cast<StagedLeaf*>(lds4);  // leaf records of the neighbour table
+  uint32_t* slot_corner = reinterpret_cast<uint32_t*>(staged + cap * 27);
+  uint32_t* brick = slot_corner + W;
+#else
+  uint32_t* slot_corner = reinterpret_cast<uint32_t*>(lds4);  // per slot: brick corner | leaf-in-block << 16
+  uint32_t* table = slot_corner + W;
   uint32_t* brick = table + cap * 27;
+#endif
   const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
@@ -454,10 +475,15 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
         s.leaf == kSentinelLeaf
             ? 0xFFFFFFFFu
             : ((s.leaf - first) << 16) | ((s.offset >> 6) * 100 + ((s.offset >> 3) & 7) * 10 + (s.offset & 7));
+    if (cached) record_leaf_xrange(g, b, s, first, xr);
   }
   const uint32_t stagers = blockDim.x > W ? blockDim.x - W : blockDim.x;
   const uint32_t stager = blockDim.x > W ? threadIdx.x - W : threadIdx.x;  // wraps for decoders when blockDim > W
+#if VBM_STAGE_LEAVES
+  if (blockDim.x == W || threadIdx.x >= W) fill_table_range_staged(g, first, count0, staged, stager, stagers);
+#else
   if (blockDim.x == W || threadIdx.x >= W) fill_table_range(g, first, count0, table, stager, stagers);
+#endif
   __syncthreads();
   if (!cached) {  // per-tap tree walk
     for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
@@ -473,12 +499,21 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   }
   for (uint32_t j0 = 0; j0 < span; j0 += cap) {
     const uint32_t count = min(cap, span - j0);
+#if VBM_STAGE_LEAVES
+    if (j0) {  // later passes: the whole block restages
+      __syncthreads();  // the previous pass is done with the LDS
+      fill_table_range_staged(g, first + j0, count, staged, threadIdx.x, blockDim.x);
+      __syncthreads();
+    }
+    build_bricks_staged(staged, count, xr + j0, side.row_bytes, kInactive, brick);
+#else
     if (j0) {  // later passes: the whole block restages
       __syncthreads();  // the previous pass is done with the LDS
       fill_table_range(g, first + j0, count, table, threadIdx.x, blockDim.x);
       __syncthreads();
     }
-    build_bricks(g, table, count, side.row_bytes, kInactive, brick);
+    build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
+#endif
     for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
       const uint32_t info = slot_corner[task / LANES];
       const uint32_t j = info >> 16;
@@ -732,18 +767,32 @@ uint32_t brick_capacity(int log2w) {
   return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_CAP_W128) : log2w == 8 ? 6u : uint32_t(VBM_CAP_W512);
 }
 
+// Brick capacity of the split-row kernel, whose staged leaf records take
+// 27 * 80 bytes of LDS per spanned leaf on top of the brick: sized so that a
+// W128 workgroup still fits eight to a CU.
+#ifndef VBM_SPLIT_CAP_W128
+#define VBM_SPLIT_CAP_W128 3
+#endif
+#ifndef VBM_SPLIT_CAP_W512
+#define VBM_SPLIT_CAP_W512 6
+#endif
+uint32_t split_capacity(int log2w) {
+  if (!VBM_STAGE_LEAVES) return brick_capacity(log2w);
+  return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_SPLIT_CAP_W128) : log2w == 8 ? 4u : uint32_t(VBM_SPLIT_CAP_W512);
+}
+
 template <bool CACHED, bool STREAM>
 struct BoxLauncher {
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
     if constexpr (CACHED && VEC && (CH == 8 || CH == 16)) {
-      const uint32_t cap = brick_capacity(g.log2w);
+      const uint32_t cap = split_capacity(g.log2w);
       const uint32_t W = 1u << g.log2w;
       const uint32_t tasks = W * (CH / 4);
       const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
       hipLaunchKernelGGL((k_box_cached_split<CH, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
-                         brick_lds_bytes(cap) + W * 4, st, g, sc, bytes, out, C, ch0, cap);
+                         split_lds_bytes(cap, W), st, g, sc, bytes, out, C, ch0, cap);
     } else if constexpr (CACHED) {
       const uint32_t cap = brick_capacity(g.log2w);
       hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(1u << g.log2w),
