@@ -100,9 +100,12 @@ BOX_FLAGS = [0, vbm.STREAMING, vbm.CACHED, vbm.CACHED | vbm.STREAMING]
 
 
 @pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube", "stress_small"])
 def test_box_filter(name, C):
-    for log2w in (7, 9):
+    # every BlockWidth: the brick capacity, the per-leaf x ranges and the number of
+    # passes per block all depend on it; stress_small has blocks spanning from one
+    # leaf to more than MaxCachedLeaves
+    for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
         sc = I.sidecar(100 + C, g.n_active, C)
         want = ref.box(sc).view(np.uint32)
