@@ -101,6 +101,33 @@ def time_launches(fn, n_sets, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_graph(fn, n_sets, steps, warmup):
+    """Mean ms per launch of fn(k), k = 0..steps-1, captured once into a HIP graph and
+    replayed: for kernels shorter than a Python launch, timing eager launches would
+    measure the host.  Returns (ms, graph) so the caller can check a replay's output."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for k in range(warmup):
+            fn(k % n_sets)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(steps):
+            fn(k % n_sets)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, graph
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,13 +244,23 @@ def main():
         t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
         rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
         # device-side metadata build (leaf directories, leafFirst, block metadata)
-        for w in (7, 9):
-            gw = grids[w]
-            t = time_launches(lambda k: vbm.build_metadata(gw), 1, 20, 5)
-            rec("build_metadata_W%d" % gw.width, t, 2 * 80 * L + (4 + gw.width // 8) * gw.n_blocks)
-        # decode: select-based vs the sweep it replaced, every width (the pages' A/B)
+        # (short kernels: timed by replaying a captured graph, see time_graph)
         lib = vbm.load_library()
         import ctypes
+        for w in (7, 9):
+            gw = grids[w]
+            total = torch.zeros(1, dtype=torch.int64, device=dev)
+
+            def meta(k, gw=gw, total=total):
+                rc = lib.vbm_build_metadata(ctypes.byref(gw.hdr), ctypes.c_void_p(gw.blob.data_ptr()),
+                                            ctypes.c_void_p(total.data_ptr()),
+                                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                assert rc == 0
+            blob0 = gw.blob.clone()
+            t, _ = time_graph(meta, 1, 20, 5)
+            assert torch.equal(gw.blob, blob0) and int(total.item()) == N, "metadata replay changed the grid"
+            rec("build_metadata_W%d" % gw.width, t, 2 * 80 * L + (4 + gw.width // 8) * gw.n_blocks)
+        # decode: select-based vs the sweep it replaced, every width (the pages' A/B)
         for w in (6, 7, 8, 9):
             gw = grids[w] if w in grids else vbm.build(coords, w, device=dev)
             lo = [torch.empty(gw.n_slots, dtype=torch.int32, device=dev) for _ in range(4)]
@@ -234,7 +271,10 @@ def main():
                             ctypes.c_void_p(lo[k].data_ptr()), ctypes.c_void_p(oo[k].data_ptr()),
                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
                     assert rc == 0
-                t = time_launches(dec, 4, 50, 15)
+                t, _ = time_graph(dec, 4, 50, 15)
+                ref_leaf, ref_off = vbm.decode(gw, sweep=(nm == "decode_sweep"))
+                assert all(torch.equal(lo[k], ref_leaf.view(torch.int32)) and
+                           torch.equal(oo[k], ref_off.view(torch.int16)) for k in range(4)), nm
                 rec("%s_W%d" % (nm, gw.width), t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
 
     traffic = counted_traffic() if (C == 16 and W == 128) else None
