@@ -81,8 +81,8 @@ def counted_traffic(path=PROFILE):
 def headline_kernel(channels):
     """Name of the kernel vbm_box_filter launches for the cached streaming box at these channels."""
     if channels in (8, 16):
-        return "k_box_cached_split<%d>" % channels
-    return "k_box_cached<%d,%s,true>" % (channels, "true" if channels % 4 == 0 else "false")
+        return "k_box_cached_split<%d, true>" % channels
+    return "k_box_cached<%d, %s, true>" % (channels, "true" if channels % 4 == 0 else "false")
 
 
 def time_launches(fn, n_sets, steps, warmup):
@@ -165,7 +165,7 @@ def main():
     C = args.channels
     log("bench: generating cfg-shell")
     coords = inputs.shell_coords(**inputs.CFG_SHELL)
-    grids = {w: vbm.build(coords, w, device=dev) for w in sorted({args.log2w, 7, 9})}
+    grids = {w: vbm.build(coords, w, device=dev) for w in sorted({args.log2w, 6, 7, 8, 9})}
     g = grids[args.log2w]
     N, L, nb, W = g.n_active, g.n_leaves, g.n_blocks, g.width
     log("bench: N=%d leaves=%d blocks=%d W=%d C=%d" % (N, L, nb, W, C))
@@ -206,8 +206,23 @@ def main():
     ab = alg_bytes_filter(N, L, nb, W, C)
     achieved = ab / (ms * 1e-3) / 1e9
     log("bench: headline %.4f ms/step, %.3e voxel*ch/s, %.1f GB/s" % (ms, value, achieved))
+    # the same launches one by one, each between its own pair of events (after the timed
+    # region): median and min per launch beside the mean above
+    fn = box_step(g, flags_cs, scs, outs)
+    pairs = []
+    for k in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(k % n_sets)
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    per_launch = {"median": round(per[len(per) // 2], 5), "min": round(per[0], 5), "max": round(per[-1], 5)}
+    log("bench: per launch median %.4f min %.4f max %.4f ms" % (per_launch["median"], per_launch["min"],
+                                                                   per_launch["max"]))
 
-    extra = {}
+    extra = {"headline_per_launch_ms": per_launch}
     if not args.no_extra:
         def rec(name, ms_, bytes_, n_work=None):
             d = {"ms": round(ms_, 5), "GBps": round(bytes_ / (ms_ * 1e-3) / 1e9, 1),
@@ -227,17 +242,20 @@ def main():
                     t = time_launches(box_step(gw, fl, s_, o_), ns_, 20, 5)
                     rec("box_%s_W%d_C%d" % (nm, gw.width, ch), t,
                         alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch), N * ch)
-            for w in (7, 9):
+            # the 7-direction consumers at every BlockWidth: Laplacian and cross sum, tree
+            # walk vs Cached, materialised vs streamed; the 19-tap axis sum at W128/W512
+            for w in (6, 7, 8, 9):
                 gw = grids[w]
                 if ch in (1, 8):
                     ab_w = alg_bytes_filter(N, L, gw.n_blocks, gw.width, ch)
-                    for fl, nm in names.items():
-                        t = time_launches(lambda k: vbm.cross_filter(gw, s_[k], fl | vbm.OP_LAPLACIAN, out=o_[k]),
-                                          ns_, 20, 5)
-                        rec("laplacian_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
-                    for fl, nm in names.items():
-                        t = time_launches(lambda k: vbm.axis_filter(gw, s_[k], fl, out=o_[k]), ns_, 20, 5)
-                        rec("axis19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
+                    for op, opn in ((vbm.OP_LAPLACIAN, "laplacian"), (0, "cross_sum")):
+                        for fl, nm in names.items():
+                            t = time_launches(lambda k: vbm.cross_filter(gw, s_[k], fl | op, out=o_[k]), ns_, 20, 5)
+                            rec("%s_%s_W%d_C%d" % (opn, nm, gw.width, ch), t, ab_w, N * ch)
+                    if w in (7, 9):
+                        for fl, nm in names.items():
+                            t = time_launches(lambda k: vbm.axis_filter(gw, s_[k], fl, out=o_[k]), ns_, 20, 5)
+                            rec("axis19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
             if ch != C:
                 del s_, o_
         # hot-cache figure (single buffer set; the Infinity Cache may serve it)
@@ -260,9 +278,14 @@ def main():
             t, _ = time_graph(meta, 1, 20, 5)
             assert torch.equal(gw.blob, blob0) and int(total.item()) == N, "metadata replay changed the grid"
             rec("build_metadata_W%d" % gw.width, t, 2 * 80 * L + (4 + gw.width // 8) * gw.n_blocks)
-        # decode: select-based vs the sweep it replaced, every width (the pages' A/B)
+        # decode: select-based vs the sweep it replaced, every width (the pages' A/B), on the
+        # cfg-shell and on the decode-stress topology (20,000 leaves, occupancy 2-100 %)
+        stress = inputs.leaf_bernoulli_coords(4, **inputs.STRESS)
+        decode_grids = [("", grids[w], N, L) for w in (6, 7, 8, 9)]
         for w in (6, 7, 8, 9):
-            gw = grids[w] if w in grids else vbm.build(coords, w, device=dev)
+            gs = vbm.build(stress, w, device=dev)
+            decode_grids.append(("_stress", gs, gs.n_active, gs.n_leaves))
+        for tag, gw, N_, L_ in decode_grids:
             lo = [torch.empty(gw.n_slots, dtype=torch.int32, device=dev) for _ in range(4)]
             oo = [torch.empty(gw.n_slots, dtype=torch.int16, device=dev) for _ in range(4)]
             for fn, nm in ((lib.vbm_decode, "decode"), (lib.vbm_decode_sweep, "decode_sweep")):
@@ -275,7 +298,7 @@ def main():
                 ref_leaf, ref_off = vbm.decode(gw, sweep=(nm == "decode_sweep"))
                 assert all(torch.equal(lo[k], ref_leaf.view(torch.int32)) and
                            torch.equal(oo[k], ref_off.view(torch.int16)) for k in range(4)), nm
-                rec("%s_W%d" % (nm, gw.width), t, alg_bytes_decode(N, L, gw.n_blocks, gw.width))
+                rec("%s%s_W%d" % (nm, tag, gw.width), t, alg_bytes_decode(N_, L_, gw.n_blocks, gw.width))
 
     traffic = counted_traffic() if (C == 16 and W == 128) else None
 
