@@ -774,7 +774,7 @@ uint32_t brick_capacity(int log2w) {
 #define VBM_SPLIT_CAP_W128 3
 #endif
 #ifndef VBM_SPLIT_CAP_W512
-#define VBM_SPLIT_CAP_W512 6
+#define VBM_SPLIT_CAP_W512 8
 #endif
 uint32_t split_capacity(int log2w) {
   if (!VBM_STAGE_LEAVES) return brick_capacity(log2w);
