@@ -758,7 +758,7 @@ int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out,
 // Brick capacity (spanned leaves resolved per pass) for BlockWidth 2^log2w:
 // one pass covers about 98% of the blocks of a sphere shell.
 #ifndef VBM_CAP_W128
-#define VBM_CAP_W128 4
+#define VBM_CAP_W128 3
 #endif
 #ifndef VBM_CAP_W512
 #define VBM_CAP_W512 8
