@@ -140,7 +140,9 @@ void vbm_free_blob(void* host_blob);
  * every leaf keeps at least one active voxel and the total stays n_active (the
  * block sections are sized by it); the new total is written to *d_total (a
  * device u64; NULL to skip) so the caller can check.  The tree sections (root,
- * upper, lower) and the leaf origins are read-only here.  Asynchronous on
+ * upper, lower) and the leaf origins are read-only here.  The jumpMap words
+ * hold the per-256-leaf partial sums of the leafFirst scan until the last
+ * kernel rewrites them, so the call needs no workspace.  Asynchronous on
  * `stream`; the blob must not be in use by other work on other streams.
  * Errors: VBM_ERR_ARG, VBM_ERR_HIP.
  */

@@ -624,34 +624,44 @@ struct MutableGrid {
   int32_t log2w;
 };
 
-// Per leaf: prefix directory, and the active count parked in `first` for the scan.
+// Per leaf: prefix directory, and the active count parked in `first` for the
+// scan; per workgroup of 256 leaves the sum of their counts, parked in
+// block_jump[workgroup] (the jumpMap words are rewritten by k_meta_blocks; they
+// number at least N / 64 >= L / 64 > L / 256).
 __global__ void __launch_bounds__(256) k_meta_counts(MutableGrid m) {
+  __shared__ uint32_t group_sum;
   const uint32_t l = blockIdx.x * blockDim.x + threadIdx.x;
-  if (l >= m.n_leaves) return;
-  Leaf& L = m.leaves[l];
-  uint32_t count = 0, lo = 0, hi = 0;
+  if (threadIdx.x == 0) group_sum = 0;
+  __syncthreads();
+  if (l < m.n_leaves) {
+    Leaf& L = m.leaves[l];
+    uint32_t count = 0, lo = 0, hi = 0;
 #pragma unroll
-  for (uint32_t w = 0; w < 8; ++w) {
-    count += __popcll(L.mask[w]);
-    if (w < 7) {  // field w at bits 9w .. 9w+8, assembled in two 32-bit halves
-      const uint32_t p = 9 * w;
-      if (p < 32) lo |= count << p;
-      if (p + 9 > 32) hi |= p < 32 ? count >> (32 - p) : count << (p - 32);
+    for (uint32_t w = 0; w < 8; ++w) {
+      count += __popcll(L.mask[w]);
+      if (w < 7) {  // field w at bits 9w .. 9w+8, assembled in two 32-bit halves
+        const uint32_t p = 9 * w;
+        if (p < 32) lo |= count << p;
+        if (p + 9 > 32) hi |= p < 32 ? count >> (32 - p) : count << (p - 32);
+      }
     }
+    L.prefix = uint64_t(lo) | (uint64_t(hi) << 32);
+    L.first = count;
+    atomicAdd(&group_sum, count);
   }
-  L.prefix = uint64_t(lo) | (uint64_t(hi) << 32);
-  L.first = count;
+  __syncthreads();
+  if (threadIdx.x == 0) m.block_jump[blockIdx.x] = group_sum;
 }
 
-// One workgroup: leaf l's count becomes leafFirst = 1 + sum of the counts of
-// leaves 0..l-1.  Each work-item owns a contiguous run of leaves.
-__global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint64_t* __restrict__ total) {
+// One workgroup: the G group sums in block_jump[0 .. G) become exclusive
+// prefix sums; *total = their sum (N).  Each work-item owns a contiguous run.
+__global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint32_t G, uint64_t* __restrict__ total) {
   __shared__ uint64_t part[1024];
   const uint32_t T = blockDim.x, t = threadIdx.x;
-  const uint32_t per = (m.n_leaves + T - 1) / T;
-  const uint32_t a = min(m.n_leaves, t * per), e = min(m.n_leaves, a + per);
+  const uint32_t per = (G + T - 1) / T;
+  const uint32_t a = min(G, t * per), e = min(G, a + per);
   uint64_t s = 0;
-  for (uint32_t l = a; l < e; ++l) s += m.leaves[l].first;
+  for (uint32_t k = a; k < e; ++k) s += m.block_jump[k];
   part[t] = s;
   __syncthreads();
   for (uint32_t d = 1; d < T; d <<= 1) {  // inclusive scan of the runs' sums
@@ -660,13 +670,30 @@ __global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint64_t* __r
     part[t] += v;
     __syncthreads();
   }
-  uint64_t run = 1 + (t ? part[t - 1] : 0);
-  for (uint32_t l = a; l < e; ++l) {
-    const uint64_t c = m.leaves[l].first;
-    m.leaves[l].first = run;
+  uint64_t run = t ? part[t - 1] : 0;
+  for (uint32_t k = a; k < e; ++k) {
+    const uint64_t c = m.block_jump[k];
+    m.block_jump[k] = run;
     run += c;
   }
   if (t == T - 1 && total) *total = part[T - 1];
+}
+
+// Per workgroup of 256 leaves: leafFirst = 1 + the group's offset + the
+// exclusive scan of the counts inside the group.
+__global__ void __launch_bounds__(256) k_meta_first(MutableGrid m) {
+  __shared__ uint32_t sums[256];
+  const uint32_t t = threadIdx.x, l = blockIdx.x * blockDim.x + t;
+  const uint32_t count = l < m.n_leaves ? uint32_t(m.leaves[l].first) : 0u;
+  sums[t] = count;
+  __syncthreads();
+  for (uint32_t d = 1; d < 256; d <<= 1) {  // inclusive scan
+    const uint32_t v = t >= d ? sums[t - d] : 0u;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
+  }
+  if (l < m.n_leaves) m.leaves[l].first = 1 + m.block_jump[blockIdx.x] + (sums[t] - count);
 }
 
 // One wave per block: the leaf owning index g0 = 1 + bW (binary search over
@@ -994,8 +1021,13 @@ extern "C" int vbm_build_metadata(const vbm_grid* grid, void* d_blob, uint64_t* 
   m.n_blocks = grid->n_blocks;
   m.log2w = grid->log2_width;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(k_meta_counts, dim3((m.n_leaves + 255) / 256), dim3(256), 0, st, m);
-  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(1024), 0, st, m, d_total);
+  const uint32_t groups = (m.n_leaves + 255) / 256;
+  // the group sums live in the jumpMap words until k_meta_blocks rewrites them
+  // (a grid with every leaf non-empty always has room: N / 64 >= L / 64 words)
+  if (uint64_t(groups) > uint64_t(m.n_blocks) << (m.log2w - 6)) return VBM_ERR_ARG;
+  hipLaunchKernelGGL(k_meta_counts, dim3(groups), dim3(256), 0, st, m);
+  hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(1024), 0, st, m, groups, d_total);
+  hipLaunchKernelGGL(k_meta_first, dim3(groups), dim3(256), 0, st, m);
   if (m.n_blocks) hipLaunchKernelGGL(k_meta_blocks, dim3(m.n_blocks), dim3(64), 0, st, m);
   return launch_status();
 }
