@@ -174,13 +174,12 @@ __device__ __forceinline__ Slot decode_slot(const DeviceGrid& g, uint32_t b, uin
   return select_in_leaf(g, g.block_first_leaf[b] + rank, idx);
 }
 
-// decode_slot for the calling work-item's own slot s = threadIdx.x of a
-// workgroup of W work-items (one wave64 per 64 slots).  The jumpMap word of
+// decode_slot for the calling work-item's own slot s (default threadIdx.x):
+// one wave64 per 64 consecutive slots, s & 63 the lane.  The jumpMap word of
 // the wave is uniform, so the rank is a scalar popcount over the earlier
 // words plus the lane's rank in its wave's word (v_mbcnt over the two halves)
 // plus the lane's own bit.
-__device__ __forceinline__ Slot decode_own_slot(const DeviceGrid& g, uint32_t b) {
-  const uint32_t s = threadIdx.x;
+__device__ __forceinline__ Slot decode_own_slot(const DeviceGrid& g, uint32_t b, uint32_t s = threadIdx.x) {
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + s;
   const uint32_t words = 1u << (g.log2w - 6);
   const uint64_t* jm = g.block_jump + uint64_t(b) * words;

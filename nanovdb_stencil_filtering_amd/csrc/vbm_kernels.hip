@@ -169,6 +169,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_PIPE_SPLIT
 #define VBM_PIPE_SPLIT 8   // taps in flight per work-item in the split-row kernel
 #endif
+#ifndef VBM_DECODE_THREADS
+#define VBM_DECODE_THREADS 512  // work-items per workgroup of k_decode (W or more)
+#endif
 #ifndef VBM_STAGE_LEAVES
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
 #endif
@@ -211,10 +214,15 @@ __host__ __device__ constexpr uint32_t split_lds_bytes(uint32_t cap, uint32_t W)
 // kernels
 // ---------------------------------------------------------------------------
 
+// A workgroup of blockDim.x >= W work-items decodes blockDim.x / W consecutive
+// blocks (fewer, larger workgroups: the kernel is short and dispatch-bound).
 __global__ void __launch_bounds__(512) k_decode(DeviceGrid g, uint32_t* __restrict__ leaf_index,
                                                 uint16_t* __restrict__ voxel_offset) {
-  const Slot s = decode_own_slot(g, blockIdx.x);
-  const uint64_t row = (uint64_t(blockIdx.x) << g.log2w) + threadIdx.x;
+  const uint32_t b = blockIdx.x * (blockDim.x >> g.log2w) + (threadIdx.x >> g.log2w);
+  if (b >= g.n_blocks) return;  // whole waves (W >= 64)
+  const uint32_t slot = threadIdx.x & ((1u << g.log2w) - 1);
+  const Slot s = decode_own_slot(g, b, slot);
+  const uint64_t row = (uint64_t(b) << g.log2w) + slot;
   leaf_index[row] = s.leaf;
   voxel_offset[row] = uint16_t(s.offset);
 }
@@ -889,8 +897,11 @@ extern "C" int vbm_decode(const vbm_grid* grid, const void* d_blob, uint32_t* d_
   if (grid->n_blocks == 0) return VBM_OK;
   if (!d_leaf_index || !d_voxel_offset) return VBM_ERR_ARG;
   const DeviceGrid g = device_grid(grid, d_blob);
-  hipLaunchKernelGGL(k_decode, dim3(g.n_blocks), dim3(1u << g.log2w), 0, static_cast<hipStream_t>(stream), g,
-                     d_leaf_index, d_voxel_offset);
+  const uint32_t W = 1u << g.log2w;
+  const uint32_t threads = W > VBM_DECODE_THREADS ? W : uint32_t(VBM_DECODE_THREADS);
+  const uint32_t per_wg = threads / W;
+  hipLaunchKernelGGL(k_decode, dim3((g.n_blocks + per_wg - 1) / per_wg), dim3(threads), 0,
+                     static_cast<hipStream_t>(stream), g, d_leaf_index, d_voxel_offset);
   return launch_status();
 }
 
