@@ -23,8 +23,12 @@
  *
  * Conventions for every entry point
  *   - Return 0 (VBM_OK) or a negative vbm_status.  Nothing throws.
- *   - Arguments are validated before any HIP call; on a validation error no
- *     work is enqueued and no output is touched.
+ *   - Arguments are validated before any launch; on a validation error no
+ *     work is enqueued and no output is touched.  Every buffer a kernel reads
+ *     or writes (blob, sidecar, outputs) must be memory the GPU can reach:
+ *     device, pinned host or managed memory (checked with
+ *     hipPointerGetAttributes); anything else, such as pageable host memory,
+ *     is refused with VBM_ERR_ARG instead of faulting the GPU.
  *   - GPU work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL = the default stream).  Nothing synchronises.  A failed
  *     launch is reported as VBM_ERR_HIP.
@@ -44,7 +48,7 @@ extern "C" {
 
 typedef enum vbm_status {
   VBM_OK = 0,
-  VBM_ERR_ARG = -1,         /* null pointer, bad width / C / shape / flags, corrupt grid header */
+  VBM_ERR_ARG = -1,         /* null or host-only pointer, bad width / C / shape / flags, corrupt grid header */
   VBM_ERR_SIZE = -2,        /* grid too large for the library's index or memory limits          */
   VBM_ERR_ALIGN = -3,       /* float buffer not 4-byte aligned                                 */
   VBM_ERR_ALIAS = -4,       /* output overlaps the sidecar (neighbours are read while writing) */

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "vbm.h"
 #include "vbm_device.hpp"
 
@@ -780,6 +782,23 @@ DeviceGrid device_grid(const vbm_grid* grid, const void* d_blob) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? VBM_OK : VBM_ERR_HIP; }
 
+// Every pointer a kernel dereferences must be memory the GPU can reach: device
+// memory, pinned host memory or managed memory.  A pageable host pointer, or
+// an address HIP does not know, would fault the GPU, so it is refused before
+// any launch.
+int check_kernel_memory(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+      (void)hipGetLastError();  // the failed query must not surface as a later launch error
+      return VBM_ERR_ARG;
+    }
+    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeHost && a.type != hipMemoryTypeManaged)
+      return VBM_ERR_ARG;
+  }
+  return VBM_OK;
+}
+
 int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out, int C) {
   if (!sc || !out || C < 1) return VBM_ERR_ARG;
   if ((grid->n_active + 1) * uint64_t(C) * 4 > kInactive) return VBM_ERR_SIZE;
@@ -896,6 +915,7 @@ extern "C" int vbm_decode(const vbm_grid* grid, const void* d_blob, uint32_t* d_
   if (rc) return rc;
   if (grid->n_blocks == 0) return VBM_OK;
   if (!d_leaf_index || !d_voxel_offset) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_leaf_index, d_voxel_offset}))) return rc;
   const DeviceGrid g = device_grid(grid, d_blob);
   const uint32_t W = 1u << g.log2w;
   const uint32_t threads = W > VBM_DECODE_THREADS ? W : uint32_t(VBM_DECODE_THREADS);
@@ -911,6 +931,7 @@ extern "C" int vbm_decode_sweep(const vbm_grid* grid, const void* d_blob, uint32
   if (rc) return rc;
   if (grid->n_blocks == 0) return VBM_OK;
   if (!d_leaf_index || !d_voxel_offset) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_leaf_index, d_voxel_offset}))) return rc;
   const DeviceGrid g = device_grid(grid, d_blob);
   hipLaunchKernelGGL(k_decode_sweep, dim3(g.n_blocks), dim3(1u << g.log2w), 0, static_cast<hipStream_t>(stream), g,
                      d_leaf_index, d_voxel_offset);
@@ -925,6 +946,7 @@ extern "C" int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int
   if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
   if (grid->n_blocks == 0) return VBM_OK;
   if (!d_taps) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_taps}))) return rc;
   const DeviceGrid g = device_grid(grid, d_blob);
   const dim3 gd(g.n_blocks), bd(1u << g.log2w);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -958,6 +980,7 @@ extern "C" int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const fl
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
   if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
     hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
@@ -990,6 +1013,7 @@ extern "C" int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const 
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
   if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_OP_LAPLACIAN)) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
     hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
@@ -1009,6 +1033,7 @@ extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const f
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
   if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
     hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
@@ -1023,6 +1048,8 @@ extern "C" int vbm_build_metadata(const vbm_grid* grid, void* d_blob, uint64_t* 
   int rc = check_grid(grid, d_blob);
   if (rc) return rc;
   if (grid->n_leaves == 0) return VBM_OK;
+  if ((rc = check_kernel_memory({d_blob}))) return rc;
+  if (d_total && (rc = check_kernel_memory({d_total}))) return rc;
   uint8_t* base = static_cast<uint8_t*>(d_blob);
   MutableGrid m;
   m.leaves = reinterpret_cast<Leaf*>(base + grid->off_leaves);

@@ -199,15 +199,33 @@ def build_metadata(grid: Grid, stream=None):
     block metadata of grid.blob on the device from its leaf masks; returns the total
     active count as a one-element int64 device tensor."""
     import torch
-    total = torch.zeros(1, dtype=torch.int64, device=grid.blob.device)
+    dev = _device(grid)
+    total = torch.zeros(1, dtype=torch.int64, device=dev)
     _check(load_library().vbm_build_metadata(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(total),
-                                             _stream_ptr(stream)), "vbm_build_metadata")
+                                             _stream_ptr(stream, dev)), "vbm_build_metadata")
     return total
 
 
-def _stream_ptr(stream):
+def _device(grid: Grid):
+    """The GPU holding the grid's blob.  Every pointer the C ABI receives must be
+    device memory of that GPU: a host pointer handed to a kernel faults the GPU, so
+    the binding refuses it here."""
+    dev = grid.blob.device
+    if dev.type != "cuda":
+        raise ValueError("the grid's blob must be on a GPU (build(..., device='cuda')), not %s" % dev)
+    return dev
+
+
+def _on(t, dev, what: str):
+    if t.device != dev:
+        raise ValueError("%s must be on the grid's device %s, not %s" % (what, dev, t.device))
+
+
+def _stream_ptr(stream, dev):
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if s.device != dev:
+        raise ValueError("the stream must belong to the grid's device %s, not %s" % (dev, s.device))
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -223,12 +241,12 @@ def decode(grid: Grid, stream=None, sweep: bool = False):
     """vbm_decode (or vbm_decode_sweep) -> (leafIndex as int32 tensor, voxelOffset as int16 tensor),
     n_blocks*W each (bit patterns of u32 / u16)."""
     import torch
-    dev = grid.blob.device
+    dev = _device(grid)
     leaf = torch.empty(grid.n_slots, dtype=torch.int32, device=dev)
     off = torch.empty(grid.n_slots, dtype=torch.int16, device=dev)
     lib = load_library()
     fn, name = (lib.vbm_decode_sweep, "vbm_decode_sweep") if sweep else (lib.vbm_decode, "vbm_decode")
-    _check(fn(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(leaf), _ptr(off), _stream_ptr(stream)), name)
+    _check(fn(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(leaf), _ptr(off), _stream_ptr(stream, dev)), name)
     return leaf, off
 
 
@@ -240,45 +258,50 @@ def decode_sweep(grid: Grid, stream=None):
 def stencil_indices(grid: Grid, shape: int, flags: int = 0, stream=None):
     """vbm_stencil_indices -> int64 tensor [n_blocks*W, shape] (u64 bit patterns)."""
     import torch
-    taps = torch.empty((grid.n_slots, shape), dtype=torch.int64, device=grid.blob.device)
+    dev = _device(grid)
+    taps = torch.empty((grid.n_slots, shape), dtype=torch.int64, device=dev)
     _check(load_library().vbm_stencil_indices(ctypes.byref(grid.hdr), _blob_ptr(grid), int(shape), int(flags),
-                                              _ptr(taps), _stream_ptr(stream)), "vbm_stencil_indices")
+                                              _ptr(taps), _stream_ptr(stream, dev)), "vbm_stencil_indices")
     return taps
 
 
 def _filter_out(grid: Grid, sidecar, out):
+    """Validate the sidecar (and out) against the grid; returns (out, device)."""
     import torch
+    dev = _device(grid)
     if sidecar.dtype != torch.float32 or sidecar.dim() != 2 or sidecar.shape[0] != grid.n_active + 1:
         raise ValueError("sidecar must be float32 [(N+1), C]")
     if not sidecar.is_contiguous():
         raise ValueError("sidecar must be contiguous")
+    _on(sidecar, dev, "the sidecar")
     if out is None:
         out = torch.empty_like(sidecar)
     elif out.shape != sidecar.shape or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor shaped like the sidecar")
-    return out
+    _on(out, dev, "out")
+    return out, dev
 
 
 def box_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, stream=None):
     """vbm_box_filter -> out float32 [(N+1), C]."""
-    out = _filter_out(grid, sidecar, out)
+    out, dev = _filter_out(grid, sidecar, out)
     _check(load_library().vbm_box_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
-                                         int(sidecar.shape[1]), int(flags), _stream_ptr(stream)), "vbm_box_filter")
+                                         int(sidecar.shape[1]), int(flags), _stream_ptr(stream, dev)), "vbm_box_filter")
     return out
 
 
 def cross_filter(grid: Grid, sidecar, flags: int = CACHED | OP_SUM, out=None, stream=None):
     """vbm_cross_filter -> out float32 [(N+1), C]."""
-    out = _filter_out(grid, sidecar, out)
+    out, dev = _filter_out(grid, sidecar, out)
     _check(load_library().vbm_cross_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
-                                           int(sidecar.shape[1]), int(flags), _stream_ptr(stream)),
+                                           int(sidecar.shape[1]), int(flags), _stream_ptr(stream, dev)),
            "vbm_cross_filter")
     return out
 
 
 def axis_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, stream=None):
     """vbm_axis_filter (19-tap axis stencil sum) -> out float32 [(N+1), C]."""
-    out = _filter_out(grid, sidecar, out)
+    out, dev = _filter_out(grid, sidecar, out)
     _check(load_library().vbm_axis_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
-                                          int(sidecar.shape[1]), int(flags), _stream_ptr(stream)), "vbm_axis_filter")
+                                          int(sidecar.shape[1]), int(flags), _stream_ptr(stream, dev)), "vbm_axis_filter")
     return out

@@ -165,6 +165,50 @@ def test_fallback_grid_spans_more_than_16_leaves():
     assert spans.max() > vbm.MAX_CACHED_LEAVES
 
 
+def test_host_tensors_are_refused():
+    """A host sidecar or output never reaches the kernels (it would fault the GPU)."""
+    g, _ = grid_pair("tiny_shell", 7)
+    sc_host = torch.zeros((g.n_active + 1, 4), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device"):
+        vbm.box_filter(g, sc_host)
+    with pytest.raises(ValueError, match="device"):
+        vbm.cross_filter(g, sc_host.cuda(), vbm.CACHED, out=torch.zeros_like(sc_host))
+
+
+def test_c_abi_refuses_pageable_host_pointers():
+    """Through the C ABI itself: a pageable host buffer (a numpy array) passed as
+    the sidecar, the output or a decode map is refused with VBM_ERR_ARG before any
+    launch (hipPointerGetAttributes reports such memory as unregistered), and the
+    output stays untouched."""
+    import ctypes
+    g, _ = grid_pair("tiny_shell", 7)
+    lib = vbm.load_library()
+    C = 4
+    dev_sc = torch.zeros((g.n_active + 1, C), dtype=torch.float32, device="cuda")
+    dev_out = torch.full_like(dev_sc, 7.0)
+    host = np.zeros((g.n_active + 1) * C, np.float32)
+    hp = ctypes.c_void_p(host.ctypes.data)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blob = ctypes.c_void_p(g.blob.data_ptr())
+    dp = ctypes.c_void_p
+    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter):
+        assert fn(ctypes.byref(g.hdr), blob, hp, dp(dev_out.data_ptr()), C, 3, st) == -1
+        assert fn(ctypes.byref(g.hdr), blob, dp(dev_sc.data_ptr()), hp, C, 3, st) == -1
+    leaf = torch.zeros(g.n_slots, dtype=torch.int32, device="cuda")
+    host_off = np.zeros(g.n_slots, np.uint16)
+    assert lib.vbm_decode(ctypes.byref(g.hdr), blob, dp(leaf.data_ptr()), dp(host_off.ctypes.data), st) == -1
+    assert lib.vbm_stencil_indices(ctypes.byref(g.hdr), blob, 27, 1, dp(np.zeros(8, np.int64).ctypes.data), st) == -1
+    host_blob = np.frombuffer(g.blob.cpu().numpy().tobytes(), np.uint8).copy()
+    assert lib.vbm_box_filter(ctypes.byref(g.hdr), dp(host_blob.ctypes.data), dp(dev_sc.data_ptr()),
+                              dp(dev_out.data_ptr()), C, 3, st) == -1
+    torch.cuda.synchronize()
+    assert bool((dev_out == 7.0).all()) and bool((leaf == 0).all()) and not host_off.any()
+    # and a valid call afterwards still works (the refused queries left no error behind)
+    assert lib.vbm_box_filter(ctypes.byref(g.hdr), blob, dp(dev_sc.data_ptr()), dp(dev_out.data_ptr()), C, 3, st) == 0
+    torch.cuda.synchronize()
+    assert bool((dev_out == 0.0).all())
+
+
 def test_empty_grid_writes_row_zero():
     g = vbm.build(np.zeros((0, 3), np.int32), 7)
     sc = torch.ones((1, 3), dtype=torch.float32, device="cuda")
