@@ -342,6 +342,40 @@ def main():
                "sample": "whole cfg-shell box filter (C=%d, N=%d), %d passes, %.1f s, single thread" %
                          (C, N, reps, t_cpu)}
         log("bench: oracle %.3e voxel*ch/s" % cpu["value"])
+        # the same single-thread oracle on the other measured steps (reported beside the
+        # GPU figures under extra, never a target)
+
+        def oracle_rate(fn, work, unit, min_s=1.0):
+            n, t = 0, 0.0
+            while t < min_s:
+                t0 = time.perf_counter()
+                fn()
+                t += time.perf_counter() - t0
+                n += 1
+            return {"value": float("%.4e" % (work * n / t)), "unit": unit, "cores": 1, "kind": "oracle",
+                    "passes": n, "seconds": round(t, 2)}
+        cpu_more = {}
+        for ch in (1, 8):
+            sc_c = inputs.sidecar(3, N, ch)
+            cpu_more["box_C%d" % ch] = oracle_rate(lambda: ref.box(sc_c), N * ch, "active-voxel*channels/s")
+            cpu_more["laplacian_C%d" % ch] = oracle_rate(lambda: ref.cross(sc_c, "laplacian"), N * ch,
+                                                         "active-voxel*channels/s")
+            cpu_more["cross_sum_C%d" % ch] = oracle_rate(lambda: ref.cross(sc_c, "sum"), N * ch,
+                                                         "active-voxel*channels/s")
+            cpu_more["axis19_C%d" % ch] = oracle_rate(lambda: ref.axis(sc_c), N * ch, "active-voxel*channels/s")
+        # the leaf / block metadata by their plain definitions (leaves, prefix
+        # directories, leafFirst, firstLeafID, jumpMap)
+        cpu_more["metadata_W128"] = oracle_rate(lambda: (ref.leaves(), ref.blocks(7)), L, "leaves/s")
+        cpu_more["metadata_W128"]["sample"] = ("leaf masks and prefix directories from the voxel list, then "
+                                               "firstLeafID and jumpMap per block (leafFirst comes with the "
+                                               "oracle's grid)")
+        cpu_more["decode_W128"] = oracle_rate(lambda: ref.decode(7), -(-N // 128) * 128, "slots/s")
+        ref_stress = oracle.OracleGrid(inputs.leaf_bernoulli_coords(4, **inputs.STRESS))
+        n_stress_slots = -(-ref_stress.n_active // 128) * 128
+        cpu_more["decode_stress_W128"] = oracle_rate(lambda: ref_stress.decode(7), n_stress_slots, "slots/s")
+        for k, v in cpu_more.items():
+            log("bench: oracle %-20s %.3e %s" % (k, v["value"], v["unit"]))
+        extra["cpu_oracle"] = cpu_more
 
     out = {
         "metric": "box-filter active-voxel*channels/s (cached streaming 27-tap box, C=%d)" % C,
