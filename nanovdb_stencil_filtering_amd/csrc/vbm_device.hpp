@@ -4,11 +4,16 @@
 // the same decode and resolvers:
 //   decode_slot            slot -> (leaf, voxel offset); thread-local, in registers
 //   resolve_tree           one tap by a root-down tree walk
-//   stage_neighbour_table  per-block LDS table of neighbour leaves (all threads)
+//   stage_neighbour_table  per-block LDS table of neighbour leaf ids (all threads)
+//   stage_neighbour_records  the same table holding the neighbour leaves'
+//                          records (masks, prefix directory, first index), so
+//                          a tap resolves from LDS alone; the library's cached
+//                          cross and axis kernels use this form
 //   for_each_box[_cached]  27 taps streamed to a callback in tap order
 //   compute_box[_cached]   27 taps materialised into an array
 //   compute_cross[_cached] 7 taps materialised into an array
-//   for_each_tap[_cached]  any shape (box, cross, 19-tap axis) streamed
+//   for_each_tap[_cached|_staged]  any shape (box, cross, 19-tap axis) streamed
+//   build_bricks[_staged]  the box kernels' dense 10^3 bricks of resolved taps
 //
 // Sources: openvdb PR #2258 "VBM select-based inverse-map decode" ("What
 // changed": rank into the jumpMap, select into the value mask guided by the
@@ -110,7 +115,9 @@ __device__ __forceinline__ uint32_t prefix_field(uint64_t dir, uint32_t k) {
 // Index of voxel offset o in leaf L, 0 if the voxel is inactive:
 // leafFirst + (active voxels in the words before o's word) + (active voxels
 // below o in its word).  32-bit operations on the two halves of the word.
-__device__ __forceinline__ uint32_t index_in_leaf(const Leaf& L, uint32_t o) {
+// R is a leaf record (Leaf) or its first 80 bytes staged in LDS (StagedLeaf).
+template <class R>
+__device__ __forceinline__ uint32_t index_in_leaf(const R& L, uint32_t o) {
   const uint32_t w = o >> 6, b = o & 63;
   const uint64_t m = L.mask[w];
   const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
@@ -344,6 +351,58 @@ __device__ __forceinline__ uint32_t resolve_cached(const DeviceGrid& g, const ui
   return ok ? idx : 0u;
 }
 
+// The first 80 bytes of a leaf record (mask words, prefix directory, first
+// index) copied to LDS as five 16-byte pieces; zeros for an absent leaf.
+struct StagedLeaf {
+  uint64_t mask[8];
+  uint64_t prefix;
+  uint64_t first;
+};
+static_assert(sizeof(StagedLeaf) == 80, "staged leaf is five 16-byte pieces");
+
+// Cached resolution with the neighbour leaves' records themselves staged in
+// LDS (mask words, prefix directory, first index; zeros for an absent leaf):
+// staged[j * DIRS + dir] for spanned leaf j, so a tap is LDS reads and
+// popcounts, with no global load before the gather's.  All threads of the
+// block; ends with a barrier.  span <= kMaxCachedLeaves.
+template <int DIRS>
+__device__ __forceinline__ void stage_neighbour_records(const DeviceGrid& g, uint32_t first_leaf, uint32_t span,
+                                                        StagedLeaf* staged) {
+  for (uint32_t e = threadIdx.x; e < span * DIRS; e += blockDim.x) {
+    const uint32_t j = e / DIRS, dir = e % DIRS;
+    int dx, dy, dz;
+    if (DIRS == 27) {
+      dx = int(dir) / 9 - 1; dy = (int(dir) / 3) % 3 - 1; dz = int(dir) % 3 - 1;
+    } else {
+      // cross order -x, -y, -z, centre, +z, +y, +x
+      const int d = int(dir);
+      const int axis = d < 3 ? d : 6 - d;  // 0 = x, 1 = y, 2 = z (3 = centre)
+      const int sign = d < 3 ? -1 : (d > 3 ? 1 : 0);
+      dx = axis == 0 ? sign : 0; dy = axis == 1 ? sign : 0; dz = axis == 2 ? sign : 0;
+    }
+    const uint32_t leaf = (dx | dy | dz) ? neighbour_leaf(g, g.leaves[first_leaf + j], dx, dy, dz) : first_leaf + j;
+    const bool ok = leaf != kNoLeaf;
+    const uint4* src = reinterpret_cast<const uint4*>(&g.leaves[ok ? leaf : first_leaf]);
+    uint4* dst = reinterpret_cast<uint4*>(staged + e);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const uint4 v = src[k];
+      dst[k] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+}
+
+// resolve_cached through the staged records.
+template <int DIRS>
+__device__ __forceinline__ uint32_t resolve_staged(const StagedLeaf* staged, uint32_t j, int x, int y, int z, int di,
+                                                   int dj, int dk) {
+  const int nx = x + di, ny = y + dj, nz = z + dk;
+  const StagedLeaf& L = staged[j * DIRS + dir_slot<DIRS>(nx >> 3, ny >> 3, nz >> 3)];
+  const uint32_t o = (uint32_t(nx) & 7) << 6 | (uint32_t(ny) & 7) << 3 | (uint32_t(nz) & 7);
+  return index_in_leaf(L, o);  // an absent leaf has an empty mask: 0
+}
+
 // ---------------------------------------------------------------------------
 // cached resolution, brick form: per spanned leaf, a dense 10^3 block of
 // resolved taps in LDS
@@ -383,14 +442,6 @@ __device__ __forceinline__ ColumnBits column_bits(const DeviceGrid& g, uint32_t 
   return ColumnBits{ok ? bits : 0u, uint32_t(L.first) + before + below};
 }
 
-// The first 80 bytes of a leaf record (mask words, prefix directory, first
-// index) copied to LDS as five 16-byte pieces; zeros for an absent leaf.
-struct StagedLeaf {
-  uint64_t mask[8];
-  uint64_t prefix;
-  uint64_t first;
-};
-static_assert(sizeof(StagedLeaf) == 80, "staged leaf is five 16-byte pieces");
 
 // column_bits on a staged leaf record (an absent leaf has an empty mask).
 __device__ __forceinline__ ColumnBits column_bits_staged(const StagedLeaf& L, uint32_t wx, uint32_t y8) {
@@ -615,6 +666,15 @@ __device__ __forceinline__ void for_each_tap_cached(const DeviceGrid& g, const u
   const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
 #pragma unroll
   for (int t = 0; t < S::kTaps; ++t) f(t, resolve_cached<S::kDirs>(g, table, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+}
+
+// Any shape: taps through the staged neighbour records, streamed to f(tap, index).
+template <class S, class F>
+__device__ __forceinline__ void for_each_tap_staged(const StagedLeaf* staged, uint32_t first_leaf, Slot s, F&& f) {
+  const uint32_t j = s.leaf - first_leaf;
+  const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+#pragma unroll
+  for (int t = 0; t < S::kTaps; ++t) f(t, resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
 }
 
 __device__ __forceinline__ void compute_cross(const DeviceGrid& g, Slot s, uint64_t (&st)[kCrossTaps]) {

@@ -309,7 +309,7 @@ __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t*
 // straight to the output row or materialised into an array first.
 template <class S, bool CACHED, bool STREAM>
 __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict__ taps) {
-  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * S::kDirs : 1];
+  __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
   const uint32_t b = blockIdx.x;
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
     first = g.block_first_leaf[b];
     const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
     if (span <= kMaxCachedLeaves) {
-      stage_neighbour_table<S::kDirs>(g, first, span, table);
+      stage_neighbour_records<S::kDirs>(g, first, span, staged);
       cached = true;
     }
   }
@@ -331,12 +331,12 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
   }
   if constexpr (STREAM) {
     auto put = [&](int t, uint32_t idx) { out[t] = idx; };
-    if (cached) for_each_tap_cached<S>(g, table, first, s, put);
+    if (cached) for_each_tap_staged<S>(staged, first, s, put);
     else for_each_tap<S>(g, s, put);
   } else {
     uint64_t st[S::kTaps];
     auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
-    if (cached) for_each_tap_cached<S>(g, table, first, s, keep);
+    if (cached) for_each_tap_staged<S>(staged, first, s, keep);
     else for_each_tap<S>(g, s, keep);
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) out[j] = st[j];
@@ -549,7 +549,7 @@ template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM>
 __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                  float* __restrict__ out, uint32_t C, uint32_t ch0) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
-  __shared__ uint32_t table[CACHED ? kMaxCachedLeaves * S::kDirs : 1];
+  __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
@@ -560,7 +560,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
     first = g.block_first_leaf[b];
     const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
     if (span <= kMaxCachedLeaves) {
-      stage_neighbour_table<S::kDirs>(g, first, span, table);
+      stage_neighbour_records<S::kDirs>(g, first, span, staged);
       cached = true;
     }
   }
@@ -576,7 +576,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
       const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
       gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
         if (LAP && t == S::kCentre) return kInactive;
-        return tap_offset(side, resolve_cached<S::kDirs>(g, table, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+        return tap_offset(side, resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
       });
     } else {
       const VoxelCoord p = voxel_coord(g, s);
@@ -588,7 +588,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
   } else {
     uint64_t st[S::kTaps];
     auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
-    if (cached) for_each_tap_cached<S>(g, table, first, s, keep);
+    if (cached) for_each_tap_staged<S>(staged, first, s, keep);
     else for_each_tap<S>(g, s, keep);
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) {
