@@ -258,6 +258,36 @@ def main():
                             rec("axis19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
             if ch != C:
                 del s_, o_
+        # the pages' resolver table, on the shell that reproduces their grid (R=160, h=2:
+        # 1,288,594 voxels, 9,140 leaves): the six resolvers at C=1 and C=8, W128 and W512,
+        # as speedups over the tree-walk materialised box (their baseline)
+        pcoords = inputs.shell_coords(**inputs.PAGES_SHELL)
+        pgrids = {w: vbm.build(pcoords, w, device=dev) for w in (7, 9)}
+        Np = pgrids[7].n_active
+        six = (("computeBoxStencil", "box", 0), ("forEachBoxStencil", "box", vbm.STREAMING),
+               ("computeBoxStencilCached", "box", vbm.CACHED), ("forEachBoxStencilCached", "box", flags_cs),
+               ("computeCrossStencil", "cross", 0), ("computeCrossStencilCached", "cross", vbm.CACHED))
+        pages_table = {}
+        for ch in (1, 8):
+            psc = torch.from_numpy(inputs.sidecar(2, Np, ch)).to(dev)
+            pn = max(2, -(-3 * MALL_BYTES // (2 * psc.numel() * 4)))
+            ps = [psc] + [psc.clone() for _ in range(pn - 1)]
+            po = [torch.empty_like(psc) for _ in range(pn)]
+            for w in (7, 9):
+                gw = pgrids[w]
+                row = {}
+                for name, op, fl in six:
+                    if op == "box":
+                        t = time_launches(lambda k: vbm.box_filter(gw, ps[k], fl, out=po[k]), pn, 30, 8)
+                    else:
+                        t = time_launches(lambda k: vbm.cross_filter(gw, ps[k], fl | vbm.OP_SUM, out=po[k]), pn, 30, 8)
+                    row[name] = t
+                base = row["computeBoxStencil"]
+                for name, t in row.items():
+                    pages_table["%s_W%d_C%d" % (name, gw.width, ch)] = {"ms": round(t, 5), "x": round(base / t, 2)}
+                    log("  pages-shell %-26s W%d C%d %.4f ms  %.2fx" % (name, gw.width, ch, t, base / t))
+            del ps, po, psc
+        extra["pages_shell_resolvers"] = pages_table
         # hot-cache figure (single buffer set; the Infinity Cache may serve it)
         t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
         rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
