@@ -174,6 +174,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_DECODE_THREADS
 #define VBM_DECODE_THREADS 512  // work-items per workgroup of k_decode (W or more)
 #endif
+#ifndef VBM_STENCIL_SPLIT
+#define VBM_STENCIL_SPLIT 1  // 1: cross / Laplacian / axis filters split 16-channel rows over 4 work-items
+#endif
 #ifndef VBM_STAGE_LEAVES
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
 #endif
@@ -625,6 +628,70 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
 // Three launches: per-leaf counts and directories, one workgroup scanning the
 // counts in place into leafFirst, one wave per block for its metadata.
 
+// The 7-direction filters with each sidecar row split over LANES = CH / 4
+// work-items (one float4 of channels each; used for CH = 16), as in
+// k_box_cached_split: the slots are decoded once into LDS (threads < W), the
+// neighbour records staged (Cached), then every (slot, quarter) task resolves
+// its taps and gathers its 16 bytes per tap in tap order.  The workgroup has at
+// least W work-items.  Same taps, same order, same result as k_stencil.
+template <class S, int CH, bool CACHED, bool LAP, bool STREAM>
+__global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                                       float* __restrict__ out, uint32_t C, uint32_t ch0) {
+  static_assert(CH % 4 == 0 && CH >= 8, "split rows need whole float4 groups");
+  constexpr uint32_t LANES = CH / 4;
+  constexpr int kPipe = VBM_PIPE_SPLIT < S::kTaps ? VBM_PIPE_SPLIT : S::kTaps;
+  __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  __shared__ uint32_t slot_info[512];  // per slot: leaf-in-block << 16 | voxel offset, or 0xFFFFFFFF
+  const uint32_t W = 1u << g.log2w;
+  const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
+  if (b >= g.n_blocks) return;  // padding workgroup
+  if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const uint32_t first = g.block_first_leaf[b];
+  const uint32_t span = block_span(g, b);  // block-uniform: the barriers below are uniform
+  const bool cached = CACHED && span <= kMaxCachedLeaves;
+  if (threadIdx.x < W) {
+    const Slot s = decode_own_slot(g, b);
+    slot_info[threadIdx.x] = s.leaf == kSentinelLeaf ? 0xFFFFFFFFu : ((s.leaf - first) << 16) | s.offset;
+  }
+  if (cached) stage_neighbour_records<S::kDirs>(g, first, span, staged);  // ends with a barrier
+  else __syncthreads();
+  for (uint32_t task = threadIdx.x; task < W * LANES; task += blockDim.x) {
+    const uint32_t info = slot_info[task / LANES];
+    if (info == 0xFFFFFFFFu) continue;
+    const uint32_t q = task % LANES, j = info >> 16, o = info & 0xFFFF;
+    const int x = int(o >> 6), y = int((o >> 3) & 7), z = int(o & 7);
+    // index of tap t ((LAP) the centre reads as inactive: it enters only as -6 * centre)
+    auto tap = [&](int t) -> uint32_t {
+      if (LAP && t == S::kCentre) return 0u;
+      if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t));
+      const Leaf& L = g.leaves[first + j];
+      return resolve_tree(g, L.origin[0] + x + S::di(t), L.origin[1] + y + S::dj(t), L.origin[2] + z + S::dk(t));
+    };
+    auto piece = [&](uint32_t idx) { return idx ? idx * side.row_bytes + 16 * q : kInactive; };
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (STREAM) {
+      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return piece(tap(t)); });
+    } else {
+      uint32_t st[S::kTaps];
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t) st[t] = tap(t);
+      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return piece(st[t]); });
+    }
+    const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + task / LANES;
+    if constexpr (LAP) {
+      float centre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      add_row<4, true>(centre, side, uint32_t(idx) * side.row_bytes + 16 * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float six_c = 6.0f * centre[c];
+        acc[c] = acc[c] - six_c;
+      }
+    }
+    reinterpret_cast<float4*>(out + idx * C + ch0)[q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
 struct MutableGrid {
   Leaf* leaves;
   uint32_t* block_first_leaf;
@@ -863,8 +930,15 @@ struct StencilLauncher {
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
-    hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g,
-                       sc, bytes, out, C, ch0);
+    if constexpr (VBM_STENCIL_SPLIT && VEC && CH == 16) {  // at CH = 8 one work-item per row is faster
+      const uint32_t W = 1u << g.log2w, tasks = W * (CH / 4);
+      const uint32_t threads = tasks < 256 ? tasks : (W > 256 ? W : 256u);
+      hipLaunchKernelGGL((k_stencil_split<S, CH, CACHED, LAP, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
+                         0, st, g, sc, bytes, out, C, ch0);
+    } else {
+      hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st,
+                         g, sc, bytes, out, C, ch0);
+    }
   }
 };
 
