@@ -117,7 +117,7 @@ def test_box_filter(name, C):
             assert np.array_equal(u32(out), want), (log2w, flags)
 
 
-@pytest.mark.parametrize("C", [1, 3, 8, 16])
+@pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
 @pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube"])
 def test_cross_filter(name, C):
     for log2w in (6, 7, 8, 9):
@@ -136,7 +136,7 @@ def test_cross_filter(name, C):
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
 @pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand"])
 def test_axis_filter(name, C):
-    for log2w in (6, 7, 9):
+    for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
         sc = I.sidecar(300 + C, g.n_active, C)
         want = ref.axis(sc).view(np.uint32)
