@@ -175,6 +175,47 @@ def test_host_tensors_are_refused():
         vbm.cross_filter(g, sc_host.cuda(), vbm.CACHED, out=torch.zeros_like(sc_host))
 
 
+@pytest.mark.parametrize("C", [8, 16, 36])
+def test_filters_on_unaligned_and_wide_buffers(C):
+    """Sidecar and output 4-byte but not 16-byte aligned take the kernels without
+    float4 loads; C = 36 runs as three channel chunks (16 + 16 + 4).  Both must
+    still match the oracle bit for bit."""
+    g, ref = grid_pair("tiny_shell", 7)
+    sc = I.sidecar(400 + C, g.n_active, C)
+    n = sc.size
+    want = {"box": ref.box(sc), "lap": ref.cross(sc, "laplacian"), "axis": ref.axis(sc)}
+    for shift in (0, 1):  # float elements: 0 = 16-byte aligned, 1 = 4-byte aligned only
+        big_in = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
+        big_in[shift:] = torch.from_numpy(sc.ravel()).cuda()
+        sct = big_in[shift:].view(g.n_active + 1, C)
+        big_out = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
+        out = big_out[shift:].view(g.n_active + 1, C)
+        assert (sct.data_ptr() % 16 == 0) == (shift == 0)
+        for flags in BOX_FLAGS:
+            say("unaligned/wide C=%d shift=%d flags=%d" % (C, shift, flags))
+            for name, run in (("box", lambda: vbm.box_filter(g, sct, flags, out=out)),
+                              ("lap", lambda: vbm.cross_filter(g, sct, flags | vbm.OP_LAPLACIAN, out=out)),
+                              ("axis", lambda: vbm.axis_filter(g, sct, flags, out=out))):
+                out.fill_(float("nan"))
+                run()
+                assert np.array_equal(u32(out), want[name].view(np.uint32)), (name, shift, flags)
+
+
+def test_c_abi_refuses_unaligned_floats():
+    """A float pointer that is not 4-byte aligned is refused (VBM_ERR_ALIGN) before any launch."""
+    import ctypes
+    g, _ = grid_pair("tiny_shell", 7)
+    lib = vbm.load_library()
+    sc = torch.zeros((g.n_active + 1) * 4 + 4, dtype=torch.float32, device="cuda")
+    out = torch.full_like(sc, 5.0)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = lib.vbm_box_filter(ctypes.byref(g.hdr), ctypes.c_void_p(g.blob.data_ptr()), ctypes.c_void_p(sc.data_ptr() + 2),
+                            ctypes.c_void_p(out.data_ptr()), 4, 3, st)
+    assert rc == -3
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
+
+
 def test_c_abi_refuses_pageable_host_pointers():
     """Through the C ABI itself: a pageable host buffer (a numpy array) passed as
     the sidecar, the output or a decode map is refused with VBM_ERR_ARG before any
