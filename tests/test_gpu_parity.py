@@ -201,6 +201,37 @@ def test_filters_on_unaligned_and_wide_buffers(C):
                 assert np.array_equal(u32(out), want[name].view(np.uint32)), (name, shift, flags)
 
 
+def test_extreme_coordinates_by_translation():
+    """Coordinates near the library's limit (|c| < 2^30): the tiny shell moved by
+    whole root tiles (4096 voxels) to within two tiles of +-2^30 on every axis.
+    Root tiles keep their order and every voxel its place inside its tile, so the
+    indices, and therefore the decode maps, the raw taps and every filter, must equal
+    the oracle's for the shell at the origin (the oracle itself stops at 2^20)."""
+    coords = I.shell_coords(**I.TINY_SHELL)
+    ref = oracle.OracleGrid(coords)
+    far = (1 << 30) - 2 * 4096
+    shift = np.array([far, -far, far], np.int64)
+    moved = (coords.astype(np.int64) + shift).astype(np.int32)
+    assert np.abs(moved.astype(np.int64)).max() < (1 << 30)
+    C = 16
+    sc = I.sidecar(500, ref.n_active, C)
+    sct = torch.from_numpy(sc).cuda()
+    for log2w in (7, 9):
+        g = vbm.build(moved, log2w)
+        assert (g.n_active, g.n_leaves) == (ref.n_active, ref.n_leaves)
+        leaf, off = vbm.decode(g)
+        rl, ro = ref.decode(log2w)
+        assert np.array_equal(u32(leaf), rl) and np.array_equal(off.cpu().numpy().view(np.uint16), ro)
+        for flags in BOX_FLAGS:
+            say("extreme coords W=%d flags=%d" % (1 << log2w, flags))
+            taps = vbm.stencil_indices(g, 27, flags).cpu().numpy().view(np.uint64)
+            assert np.array_equal(taps[:ref.n_active], ref.taps(27).astype(np.uint64)), flags
+            assert np.array_equal(u32(vbm.box_filter(g, sct, flags)), ref.box(sc).view(np.uint32)), flags
+            lap = vbm.cross_filter(g, sct, flags | vbm.OP_LAPLACIAN)
+            assert np.array_equal(u32(lap), ref.cross(sc, "laplacian").view(np.uint32)), flags
+            assert np.array_equal(u32(vbm.axis_filter(g, sct, flags)), ref.axis(sc).view(np.uint32)), flags
+
+
 def test_c_abi_refuses_unaligned_floats():
     """A float pointer that is not 4-byte aligned is refused (VBM_ERR_ALIGN) before any launch."""
     import ctypes
