@@ -145,8 +145,9 @@ def main():
                     help="profile mode: time a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the VBM pipeline here is a single-GPU build "
-              "(see the sharding note in DESIGN.md); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py runs on one GPU only: the library drives a single device, and a sharded run "
+              "(contiguous block ranges per GPU plus a halo exchange) is not implemented; --gpus %d is "
+              "not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch

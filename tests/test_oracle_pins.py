@@ -215,7 +215,8 @@ def test_linear_field_identities_on_cfg_shell():
     taps = g.taps(27)
     full = (taps != 0).all(axis=1)
     faces = (taps[:, [4, 10, 12, 14, 16, 22]] != 0).all(axis=1)
-    # survey-time counts of fully surrounded voxels on this shell
+    # counts of fully surrounded voxels on this shell, from an independent numpy
+    # enumeration of the shell's neighbourhoods
     assert int(full.sum()) == 53406 and int(faces.sum()) == 575546
     box = g.box(sc)[1:, 0]
     lap = g.cross(sc, "laplacian")[1:, 0]
