@@ -177,6 +177,9 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #ifndef VBM_STENCIL_SPLIT
 #define VBM_STENCIL_SPLIT 1  // 1: cross / Laplacian / axis filters split 16-channel rows over 4 work-items
 #endif
+#ifndef VBM_PREFETCH_AHEAD
+#define VBM_PREFETCH_AHEAD 224  // split box: blocks ahead (per XCD) whose own rows each workgroup touches; 0 = off
+#endif
 #ifndef VBM_STAGE_LEAVES
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
 #endif
@@ -457,6 +460,24 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
   const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  // Touch the own rows of the block this XCD starts about one round of resident
+  // workgroups later, so that block finds them in the L2 / Infinity Cache instead
+  // of HBM.  The values are consumed only at the very end (no wave waits for them).
+  f32x4 ahead[2];
+  {
+    const uint32_t per = (g.n_blocks + 7) / 8;
+    const uint32_t in_xcd = b - (blockIdx.x % 8) * per;
+    const bool has = VBM_PREFETCH_AHEAD > 0 && in_xcd + VBM_PREFETCH_AHEAD < per;
+    const uint32_t bn = b + VBM_PREFETCH_AHEAD;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t piece = threadIdx.x + k * blockDim.x;  // 16-byte pieces of the block's W rows
+      const uint64_t row = 1 + (uint64_t(bn) << g.log2w) + piece / LANES;
+      const uint32_t off = has && piece < W * LANES && row <= g.n_active
+                               ? uint32_t(row) * side.row_bytes + 16 * (piece % LANES) : kInactive;
+      ahead[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, off, 0, 0));
+    }
+  }
   const uint32_t first = g.block_first_leaf[b];
   const uint32_t span = block_span(g, b);  // block-uniform: every barrier below is uniform
   const uint32_t tasks = W * LANES;
@@ -542,6 +563,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       }
     }
   }
+  asm volatile("" :: "v"(ahead[0]), "v"(ahead[1]));  // keeps the touch loads
 }
 
 // Filters of the 7-direction shapes: the cross (sum, or 7-point Laplacian =
