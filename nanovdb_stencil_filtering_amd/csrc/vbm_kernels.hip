@@ -178,7 +178,7 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 #define VBM_STENCIL_SPLIT 1  // 1: cross / Laplacian / axis filters split 16-channel rows over 4 work-items
 #endif
 #ifndef VBM_PREFETCH_AHEAD
-#define VBM_PREFETCH_AHEAD 224  // split box: blocks ahead (per XCD) whose own rows each workgroup touches; 0 = off
+#define VBM_PREFETCH_AHEAD 64  // split box: blocks ahead (per XCD) whose own rows each workgroup touches; 0 = off
 #endif
 #ifndef VBM_STAGE_LEAVES
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
@@ -460,9 +460,11 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
   const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
-  // Touch the own rows of the block this XCD starts about one round of resident
-  // workgroups later, so that block finds them in the L2 / Infinity Cache instead
-  // of HBM.  The values are consumed only at the very end (no wave waits for them).
+  // Touch the own rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks
+  // later (about two per CU), so that block finds them in the L2 instead of HBM;
+  // near enough that they are still in the 4 MB L2 when it starts, far enough
+  // that the loads have landed.  The values are consumed only at the very end
+  // (no wave waits for them).
   f32x4 ahead[2];
   {
     const uint32_t per = (g.n_blocks + 7) / 8;
