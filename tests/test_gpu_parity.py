@@ -73,7 +73,7 @@ def test_decode(name, log2w):
         assert np.array_equal(off.cpu().numpy().view(np.uint16), ro), sweep
 
 
-@pytest.mark.parametrize("log2w", [6, 7, 9])
+@pytest.mark.parametrize("log2w", [6, 7, 8, 9])
 @pytest.mark.parametrize("name", sorted(GRIDS))
 def test_stencil_indices(name, log2w):
     g, ref = grid_pair(name, log2w)
@@ -321,7 +321,7 @@ def _scribble_metadata(g):
     g.blob[h.off_block_jump:h.off_block_jump + nb * W // 8] = 0xC3
 
 
-@pytest.mark.parametrize("log2w", [6, 7, 9])
+@pytest.mark.parametrize("log2w", [6, 7, 8, 9])
 @pytest.mark.parametrize("name", sorted(GRIDS))
 def test_build_metadata_equals_host(name, log2w):
     coords = GRIDS[name]()
