@@ -137,7 +137,7 @@ def main():
     ap.add_argument("--log2w", type=int, default=7)
     ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="profile mode: run only this variant (e.g. box_cs) and exit")
+    ap.add_argument("--only", default="", help="profile mode: run only this variant (box_cs, box_c, box_s, box_p, decode, decode_sweep) and exit")
     ap.add_argument("--band", action="store_true",
                     help="also time the cached streaming box filter on the ~27M-voxel noisy narrow band "
                          "(W512, C=16; about a minute of set-up)")
@@ -188,7 +188,10 @@ def main():
     if args.only:
         # profiling mode: one variant, plain launches, no CPU leg
         variants = {"box_cs": flags_cs, "box_c": vbm.CACHED, "box_s": vbm.STREAMING, "box_p": 0}
-        fn = box_step(g, variants[args.only], scs, outs)
+        if args.only in ("decode", "decode_sweep"):
+            fn = lambda k: vbm.decode(g, sweep=args.only == "decode_sweep")
+        else:
+            fn = box_step(g, variants[args.only], scs, outs)
         ms = time_launches(fn, n_sets, args.steps, args.warmup)
         log("only %s: %.4f ms/launch" % (args.only, ms))
         return
