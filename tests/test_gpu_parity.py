@@ -386,3 +386,26 @@ def test_build_metadata_after_in_place_edit():
         sc = I.sidecar(77, hdr.n_active, 4)
         out = vbm.box_filter(g, torch.from_numpy(sc).cuda(), vbm.CACHED | vbm.STREAMING)
         assert np.array_equal(u32(out), ref.box(sc).view(np.uint32))
+
+
+def test_filters_on_two_streams_interleaved():
+    """The library keeps no state between calls: box filters of two sidecars
+    (16 and 3 channels, so the split and the narrow kernels) launched
+    alternately on two streams each give their own oracle result."""
+    g, ref = grid_pair("stress_small", 7)
+    sa, sb = I.sidecar(401, g.n_active, 16), I.sidecar(402, g.n_active, 3)
+    wa, wb = ref.box(sa).view(np.uint32), ref.box(sb).view(np.uint32)
+    ta, tb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    outs_a = [torch.full_like(ta, float("nan")) for _ in range(3)]
+    outs_b = [torch.full_like(tb, float("nan")) for _ in range(3)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    say("two streams: stress_small W=128, C=16 and C=3, 3 launches each")
+    for k in range(3):
+        vbm.box_filter(g, ta, vbm.CACHED | vbm.STREAMING, out=outs_a[k], stream=s1)
+        vbm.box_filter(g, tb, vbm.CACHED | vbm.STREAMING, out=outs_b[k], stream=s2)
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert np.array_equal(u32(outs_a[k]), wa), k
+        assert np.array_equal(u32(outs_b[k]), wb), k
