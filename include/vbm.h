@@ -206,7 +206,9 @@ int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int shape, int
  *   flags      VBM_CACHED | VBM_STREAMING in any combination (the four resolvers of
  *              openvdb PR #2263, "Summary" table)
  * All four variants give bit-identical outputs.
- * Errors: VBM_ERR_ARG, VBM_ERR_ALIGN, VBM_ERR_ALIAS, VBM_ERR_HIP.
+ * Errors: VBM_ERR_ARG, VBM_ERR_ALIGN, VBM_ERR_ALIAS, VBM_ERR_HIP, and VBM_ERR_SIZE
+ * when (N+1) * C * 4 bytes reach 0xFFFFFF00 (sidecar offsets are 32-bit; the
+ * offsets above that mark inactive taps).
  */
 int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                    int flags, void* stream);
@@ -222,7 +224,7 @@ int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_side
  *   "Notes", leaves out as a wash on its hardware); without it the taps are
  *   materialised (7 entries) first.  All forms give identical bits.
  * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
- * VBM_ERR_ALIAS, VBM_ERR_HIP.
+ * VBM_ERR_ALIAS, VBM_ERR_HIP, VBM_ERR_SIZE (as vbm_box_filter).
  */
 int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                      int flags, void* stream);
@@ -236,7 +238,7 @@ int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_si
  *   flags: VBM_CACHED (table of the 7 leaf directions: a reach of 3 < 8 leaves
  *   the leaf in at most one axis) and VBM_STREAMING.  All forms give identical bits.
  * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
- * VBM_ERR_ALIAS, VBM_ERR_HIP.
+ * VBM_ERR_ALIAS, VBM_ERR_HIP, VBM_ERR_SIZE (as vbm_box_filter).
  */
 int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                     int flags, void* stream);
