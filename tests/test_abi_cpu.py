@@ -123,3 +123,5 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
         assert fn(h, FAKE_DEV, sc, sc, 4, 0, None) == ALIAS
         assert fn(h, FAKE_DEV, sc, sc + 4 * N * 4, 4, 0, None) == ALIAS   # tail overlap
         assert fn(h, FAKE_DEV, sc + 4 * N * 4, sc, 4, 0, None) == ALIAS   # head overlap
+        # (N+1) * C * 4 bytes past the 32-bit sidecar offsets
+        assert fn(h, FAKE_DEV, sc, out_far, 200000, 0, None) == SIZE
