@@ -15,9 +15,12 @@ whose total size exceeds three times the cache.
 
 Printed (stdout, one JSON line): value = active-voxel*channels per second,
 the roofline object for this kernel (algorithmic bytes per launch / mean
-launch time vs 8 TB/s), the CPU oracle baseline on the host, and extra
-measurements (other resolvers, channel counts, widths, the decode, the
-Laplacian) under "extra".  Progress goes to stderr.
+launch time vs 8 TB/s), the CPU oracle baseline on the host (with the host's
+CPU model and thread counts), the decode metric (select-based decode at
+BlockWidth 128, ms), the noisy narrow band (cached streaming box, W512, C=16;
+skipped with --no-band) and extra measurements (other resolvers, channel
+counts, widths, the decode, the Laplacian) under "extra".  Progress goes to
+stderr.
 """
 import argparse
 import json
@@ -49,6 +52,24 @@ def alg_bytes_decode(n_active, n_leaves, n_blocks, width):
     """Decode: 6 B written per slot (u32 + u16), leaf mask/prefix/first (80 B),
     block metadata."""
     return 6 * n_blocks * width + 80 * n_leaves + (4 + width // 8) * n_blocks
+
+
+def host_cpu():
+    """Model string of the host CPU and the thread counts the machine reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"model": model, "hardware_concurrency": os.cpu_count(), "usable_cpus": usable}
 
 
 def kernel_sources_sha256():
@@ -138,9 +159,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="profile mode: run only this variant (box_cs, box_c, box_s, box_p, decode, decode_sweep) and exit")
-    ap.add_argument("--band", action="store_true",
-                    help="also time the cached streaming box filter on the ~27M-voxel noisy narrow band "
-                         "(W512, C=16; about a minute of set-up)")
+    ap.add_argument("--no-band", action="store_true",
+                    help="skip the ~27M-voxel noisy narrow band (cached streaming box, W512, C=16; "
+                         "about a minute of set-up), which is timed by default")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="profile mode: time a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -336,7 +357,25 @@ def main():
 
     traffic = counted_traffic() if (C == 16 and W == 128) else None
 
-    if args.band:
+    # the pages' decode metric: ms of the select-based decode at BlockWidth 128 on the
+    # cfg-shell (graph-replayed: the kernel is shorter than an eager Python launch)
+    decode_ms = extra.get("decode_W128", {}).get("ms")
+    if decode_ms is None:
+        import ctypes
+        lib = vbm.load_library()
+        g7 = grids[7]
+        lo = [torch.empty(g7.n_slots, dtype=torch.int32, device=dev) for _ in range(4)]
+        oo = [torch.empty(g7.n_slots, dtype=torch.int16, device=dev) for _ in range(4)]
+
+        def dec(k):
+            rc = lib.vbm_decode(ctypes.byref(g7.hdr), ctypes.c_void_p(g7.blob.data_ptr()),
+                                ctypes.c_void_p(lo[k].data_ptr()), ctypes.c_void_p(oo[k].data_ptr()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            assert rc == 0
+        decode_ms = round(time_graph(dec, 4, 50, 15)[0], 5)
+
+    band = None
+    if not args.no_band:
         # configuration 5: noisy narrow band, W512, C=16 (a measurement, not the headline)
         del scs, outs
         log("bench: generating the narrow band")
@@ -350,12 +389,16 @@ def main():
             b = min(Nb + 1, a + step)
             scb[a:b] = torch.from_numpy(inputs.sidecar_rows(6, a, b, 16)).to(dev)
         outb = torch.empty_like(scb)
+        # the band's sidecar and output (1.7 GB each) exceed the Infinity Cache several times
+        # over, so one buffer set already reaches every launch from HBM
         tb = time_launches(lambda k: vbm.box_filter(gb, scb, flags_cs, out=outb), 1, 10, 3)
         abb = alg_bytes_filter(Nb, gb.n_leaves, gb.n_blocks, gb.width, 16)
-        extra["band_box_cached_streaming_W512_C16"] = {
+        band = {
             "ms": round(tb, 4), "GBps": round(abb / (tb * 1e-3) / 1e9, 1),
             "hbm_frac": round(abb / (tb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "voxel_ch_per_s": float("%.4e" % (Nb * 16 / (tb * 1e-3))), "n_active": Nb}
+            "voxel_ch_per_s": float("%.4e" % (Nb * 16 / (tb * 1e-3))), "n_active": Nb, "n_leaves": gb.n_leaves,
+            "kernel": headline_kernel(16), "alg_bytes_per_launch": abb}
+        extra["band_box_cached_streaming_W512_C16"] = band
         log("  band box cached streaming W512 C16: %.4f ms, %.1f GB/s" % (tb, abb / (tb * 1e-3) / 1e9))
         del scb, outb, gb
 
@@ -374,7 +417,8 @@ def main():
         cpu = {"value": float("%.4e" % (N * C * reps / t_cpu)), "unit": "active-voxel*channels/s", "cores": 1,
                "kind": "oracle",
                "sample": "whole cfg-shell box filter (C=%d, N=%d), %d passes, %.1f s, single thread" %
-                         (C, N, reps, t_cpu)}
+                         (C, N, reps, t_cpu),
+               "host": host_cpu()}
         log("bench: oracle %.3e voxel*ch/s" % cpu["value"])
         # the same single-thread oracle on the other measured steps (reported beside the
         # GPU figures under extra, never a target)
@@ -432,6 +476,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": ab, "kernel": headline_kernel(C)},
         "cpu_baseline": cpu,
+        "decode_ms_W128": decode_ms,
+        "band": band,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)

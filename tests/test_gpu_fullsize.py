@@ -2,10 +2,13 @@
 benchmark times (no CPU fallback: every output comes from the HIP path).
 
 * sphere shell R=185, |d| <= 1.5 (1,290,538 voxels), the benchmark workload:
-  full decode maps at W128 / W512 against the oracle; the cached streaming box
-  filter at C=16 (the benchmark's sidecar) on sampled rows against the oracle,
-  and the other resolvers bitwise against it over every row; the Laplacian and
-  the 19-tap axis filter at C=8 on sampled rows;
+  decode maps at every BlockWidth; the 27-tap box filter at C in {1, 3, 8, 16}
+  (16 is the benchmark's sidecar) with all four resolver / delivery flags at
+  W128 and W512; the cross sum and the 7-point Laplacian at C in {1, 8} with
+  all four flags at W64, W128, W256 and W512; the 19-tap axis filter at C=8.
+  Every output row is compared bit for bit with the oracle's whole-grid result
+  (the oracle filters the shell in about a second).  Outputs are prefilled
+  with NaN so a row the kernel skips cannot pass;
 * decode stress (20,000 random leaves, Bernoulli masks): full decode maps,
   select and sweep, every width, against the oracle, partial last block and
   sentinels included;
@@ -34,6 +37,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 from nanovdb_stencil_filtering_amd import vbm  # noqa: E402
 
 CS = vbm.CACHED | vbm.STREAMING
+FLAGS = [0, vbm.STREAMING, vbm.CACHED, CS]
 
 
 def say(msg):
@@ -56,43 +60,74 @@ def sample_rows(n_active, width, k, seed):
 @pytest.fixture(scope="module")
 def shell():
     coords = I.shell_coords(**I.CFG_SHELL)
-    return coords, oracle.OracleGrid(coords)
+    ref = oracle.OracleGrid(coords)
+    grids = {w: vbm.build(coords, w) for w in (6, 7, 8, 9)}
+    g = grids[7]
+    assert g.n_active == 1290538 and g.n_leaves == 11255 and ref.n_active == g.n_active
+    return ref, grids
 
 
-@pytest.mark.parametrize("log2w", [7, 9])
-def test_cfg_shell_bench_config(shell, log2w):
-    coords, ref = shell
-    g = vbm.build(coords, log2w)
-    N = g.n_active
-    assert N == 1290538 and g.n_leaves == 11255
+def compare_every_row(run, sct, want, what):
+    """Run one filter into a NaN-filled output and compare all (N+1)*C words."""
+    say(what)
+    out = torch.full_like(sct, float("nan"))
+    run(out)
+    got = u32(out)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, "%s: %d rows differ, first %s" % (what, bad.size, bad[:8].tolist())
+
+
+@pytest.mark.parametrize("log2w", [6, 7, 8, 9])
+def test_cfg_shell_decode(shell, log2w):
+    ref, grids = shell
+    g = grids[log2w]
     say("cfg-shell W=%d decode" % g.width)
     leaf, off = vbm.decode(g)
     rl, ro = ref.decode(log2w)
     assert np.array_equal(leaf.cpu().numpy().view(np.uint32), rl)
     assert np.array_equal(off.cpu().numpy().view(np.uint16), ro)
-    del leaf, off
-    sc = I.sidecar(2, N, 16)   # the benchmark's sidecar
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 16])
+def test_cfg_shell_box_every_row(shell, C):
+    ref, grids = shell
+    N = grids[7].n_active
+    sc = I.sidecar(2, N, C)   # seed 2: the benchmark's sidecar
+    want = ref.box(sc).view(np.uint32)
     sct = torch.from_numpy(sc).cuda()
-    say("cfg-shell W=%d box C=16 cached streaming" % g.width)
-    head = vbm.box_filter(g, sct, CS)
-    rows = sample_rows(N, g.width, 4096, 10 + log2w)
-    got = u32(head)[rows.astype(np.int64)]
-    assert np.array_equal(got, ref.box(sc, rows).view(np.uint32))
-    assert np.all(u32(head)[0] == 0)
-    for flags in (0, vbm.STREAMING, vbm.CACHED):
-        say("cfg-shell W=%d box C=16 flags=%d" % (g.width, flags))
-        other = vbm.box_filter(g, sct, flags)
-        assert torch.equal(other.view(torch.int32), head.view(torch.int32)), flags
-    del sct, head
-    sc8 = I.sidecar(3, N, 8)
-    sct8 = torch.from_numpy(sc8).cuda()
-    rows = sample_rows(N, g.width, 2048, 20 + log2w)
-    ri = rows.astype(np.int64)
-    say("cfg-shell W=%d laplacian/axis C=8" % g.width)
-    lap = u32(vbm.cross_filter(g, sct8, vbm.CACHED | vbm.OP_LAPLACIAN))
-    assert np.array_equal(lap[ri], ref.cross(sc8, "laplacian", rows).view(np.uint32))
-    ax = u32(vbm.axis_filter(g, sct8, CS))
-    assert np.array_equal(ax[ri], ref.axis(sc8, rows).view(np.uint32))
+    for log2w in (7, 9):
+        g = grids[log2w]
+        for flags in FLAGS:
+            compare_every_row(lambda out: vbm.box_filter(g, sct, flags, out=out), sct, want,
+                              "cfg-shell box W=%d C=%d flags=%d" % (g.width, C, flags))
+
+
+@pytest.mark.parametrize("C", [1, 8])
+def test_cfg_shell_cross_every_row(shell, C):
+    ref, grids = shell
+    N = grids[7].n_active
+    sc = I.sidecar(3, N, C)
+    sct = torch.from_numpy(sc).cuda()
+    for op, code in (("sum", vbm.OP_SUM), ("laplacian", vbm.OP_LAPLACIAN)):
+        want = ref.cross(sc, op).view(np.uint32)
+        for log2w in (6, 7, 8, 9):
+            g = grids[log2w]
+            for flags in FLAGS:
+                compare_every_row(lambda out: vbm.cross_filter(g, sct, flags | code, out=out), sct, want,
+                                  "cfg-shell cross %s W=%d C=%d flags=%d" % (op, g.width, C, flags))
+
+
+def test_cfg_shell_axis_every_row(shell):
+    ref, grids = shell
+    N = grids[7].n_active
+    sc = I.sidecar(4, N, 8)
+    sct = torch.from_numpy(sc).cuda()
+    want = ref.axis(sc).view(np.uint32)
+    for log2w in (7, 9):
+        g = grids[log2w]
+        for flags in FLAGS:
+            compare_every_row(lambda out: vbm.axis_filter(g, sct, flags, out=out), sct, want,
+                              "cfg-shell axis W=%d C=8 flags=%d" % (g.width, flags))
 
 
 def test_decode_stress_full():
