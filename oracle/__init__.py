@@ -69,8 +69,17 @@ def _load():
     lib.oracle_cross_filter.argtypes = [P, P, I32, I32, P]
     lib.oracle_axis_rows.argtypes = [P, P, I32, P, I64, P]
     lib.oracle_axis_filter.argtypes = [P, P, I32, P]
+    lib.oracle_weno_rows.argtypes = [P, P, I32, P, I64, P]
+    lib.oracle_weno_filter.argtypes = [P, P, I32, P]
+    lib.oracle_weno5.restype = ctypes.c_float
+    lib.oracle_weno5.argtypes = [ctypes.c_float] * 5
     _lib = lib
     return lib
+
+
+def weno5(a: float, b: float, c: float, d: float, e: float) -> float:
+    """The oracle's fifth-order WENO derivative from five differences (fp32)."""
+    return float(_load().oracle_weno5(a, b, c, d, e))
 
 
 def _ptr(a: np.ndarray):
@@ -176,4 +185,20 @@ class OracleGrid:
         idx = np.ascontiguousarray(idx, dtype=np.uint64)
         out = np.empty((idx.size, C), np.float32)
         self._lib.oracle_axis_rows(self._h, _ptr(sc), C, _ptr(idx), idx.size, _ptr(out))
+        return out
+
+    def weno(self, sidecar: np.ndarray, idx: np.ndarray | None = None) -> np.ndarray:
+        """WENO consumer on the 19 axis taps: per channel the squared norm of the
+        Godunov upwind gradient from fifth-order WENO one-sided derivatives (fp32).
+        Inactive taps read sidecar row 0."""
+        sc = np.ascontiguousarray(sidecar, dtype=np.float32)
+        C = sc.shape[1]
+        assert sc.shape[0] == self.n_active + 1
+        if idx is None:
+            out = np.empty((self.n_active + 1, C), np.float32)
+            self._lib.oracle_weno_filter(self._h, _ptr(sc), C, _ptr(out))
+            return out
+        idx = np.ascontiguousarray(idx, dtype=np.uint64)
+        out = np.empty((idx.size, C), np.float32)
+        self._lib.oracle_weno_rows(self._h, _ptr(sc), C, _ptr(idx), idx.size, _ptr(out))
         return out

@@ -50,7 +50,15 @@
 //    its consumer accumulates the 19 taps like the box and cross consumers;
 //  * box filter = plain sum (no division); cross sum = sum over 7 taps;
 //    7-point Laplacian = (sum of the active face taps, in cross order) minus
-//    the separately rounded product 6*centre.
+//    the separately rounded product 6*centre;
+//  * WENO consumer on the 19 axis taps (the pages name it, without its
+//    arithmetic): per channel the squared norm of the Godunov upwind gradient
+//    built from fifth-order WENO one-sided derivatives (Jiang and Shu,
+//    "Efficient implementation of weighted ENO schemes", J. Comput. Phys. 126,
+//    1996; the Hamilton-Jacobi form of Jiang and Peng, SIAM J. Sci. Comput. 21,
+//    2000), unit voxel spacing, epsilon 1e-6.  An inactive tap takes the value
+//    of sidecar row 0 (index 0, the background).  The fp32 evaluation order is
+//    fixed operation by operation in weno5() and weno_norm_sq() below.
 
 #include <algorithm>
 #include <array>
@@ -127,6 +135,41 @@ std::vector<Coord> axis19_offsets() {
       for (int dk = -3; dk <= 3; ++dk)
         if ((di != 0) + (dj != 0) + (dk != 0) <= 1) v.push_back({di, dj, dk});
   return v;
+}
+
+// Fifth-order WENO one-sided derivative from five consecutive differences
+// a..e of the field along one axis, ordered away from the upwind side (for the
+// left-biased derivative a = u[-2]-u[-3], ..., e = u[2]-u[1]).  Three
+// third-order candidates, their smoothness indicators, and the nonlinear
+// weights built from the ideal weights 1/10, 6/10, 3/10 (scaled by 10, which
+// the normalisation removes) as in Jiang and Shu (1996), section 2.  Every
+// operation is one fp32 rounding in the order written.
+float weno5(float a, float b, float c, float d, float e) {
+  const float eps = 1.0e-6f;
+  // candidate derivatives on the three sub-stencils
+  const float p1 = ((2.0f * a - 7.0f * b) + 11.0f * c) / 6.0f;
+  const float p2 = ((-b + 5.0f * c) + 2.0f * d) / 6.0f;
+  const float p3 = ((2.0f * c + 5.0f * d) - e) / 6.0f;
+  // smoothness indicators: 13/12 (second difference)^2 + 1/4 (first-order term)^2
+  const float q1 = (a - 2.0f * b) + c, r1 = (a - 4.0f * b) + 3.0f * c;
+  const float q2 = (b - 2.0f * c) + d, r2 = b - d;
+  const float q3 = (c - 2.0f * d) + e, r3 = (3.0f * c - 4.0f * d) + e;
+  const float s1 = (13.0f * (q1 * q1)) / 12.0f + (r1 * r1) * 0.25f;
+  const float s2 = (13.0f * (q2 * q2)) / 12.0f + (r2 * r2) * 0.25f;
+  const float s3 = (13.0f * (q3 * q3)) / 12.0f + (r3 * r3) * 0.25f;
+  const float t1 = s1 + eps, t2 = s2 + eps, t3 = s3 + eps;
+  const float w1 = 1.0f / (t1 * t1), w2 = 6.0f / (t2 * t2), w3 = 3.0f / (t3 * t3);
+  return ((w1 * p1 + w2 * p2) + w3 * p3) / ((w1 + w2) + w3);
+}
+
+// Godunov's upwind choice for |grad u|^2 along one axis from the left- and
+// right-biased derivatives dm, dp; `outside` (centre value > 0) selects the
+// branch for motion along +grad u, otherwise along -grad u.
+float godunov_sq(float dm, float dp, bool outside) {
+  const float lo = outside ? (dm > 0.0f ? dm : 0.0f) : (dm < 0.0f ? dm : 0.0f);
+  const float hi = outside ? (dp < 0.0f ? dp : 0.0f) : (dp > 0.0f ? dp : 0.0f);
+  const float a = lo * lo, b = hi * hi;
+  return a > b ? a : b;
 }
 
 uint64_t lookup(const Grid& g, const Coord& q) {
@@ -316,6 +359,45 @@ void oracle_axis_rows(const void* h, const float* sidecar, int C, const uint64_t
   }
 }
 
+// WENO consumer for the m indices in idx[]: out[i*C + ch] = squared norm of
+// the Godunov upwind gradient of channel ch at voxel idx[i].  Per axis the
+// seven values u[-3..3] come from the voxel's axis taps (an inactive tap reads
+// sidecar row 0); the six differences d[k] = u[k] - u[k-1], k = -2..3, give
+// the left-biased derivative weno5(d[-2], d[-1], d[0], d[1], d[2]) and the
+// right-biased one weno5(d[3], d[2], d[1], d[0], d[-1]); the axes are summed
+// x, then y, then z.
+void oracle_weno_rows(const void* h, const float* sidecar, int C, const uint64_t* idx, int64_t m, float* out) {
+  const Grid& g = *static_cast<const Grid*>(h);
+  for (int64_t i = 0; i < m; ++i) {
+    const Coord& p = g.voxel[idx[i] - 1];
+    uint64_t tap[3][7];  // [axis][k + 3]
+    for (int axis = 0; axis < 3; ++axis)
+      for (int k = -3; k <= 3; ++k) {
+        Coord q = p;
+        if (axis == 0) q.x += k;
+        if (axis == 1) q.y += k;
+        if (axis == 2) q.z += k;
+        tap[axis][k + 3] = lookup(g, q);
+      }
+    for (int ch = 0; ch < C; ++ch) {
+      const float centre = sidecar[idx[i] * uint64_t(C) + uint64_t(ch)];
+      const bool outside = centre > 0.0f;
+      float sum = 0.0f;
+      for (int axis = 0; axis < 3; ++axis) {
+        float u[7];
+        for (int k = 0; k < 7; ++k) u[k] = sidecar[tap[axis][k] * uint64_t(C) + uint64_t(ch)];  // index 0: row 0
+        float d[6];  // d[j] = u[j+1] - u[j], i.e. the differences k = -2..3
+        for (int j = 0; j < 6; ++j) d[j] = u[j + 1] - u[j];
+        const float dm = weno5(d[0], d[1], d[2], d[3], d[4]);
+        const float dp = weno5(d[5], d[4], d[3], d[2], d[1]);
+        const float gsq = godunov_sq(dm, dp, outside);
+        sum = axis == 0 ? gsq : sum + gsq;
+      }
+      out[i * C + ch] = sum;
+    }
+  }
+}
+
 // Box filter for the m indices in idx[]: out[i*C + ch] = fp32 sum, in tap
 // order, of sidecar[tap*C + ch] over the active taps of voxel idx[i].
 void oracle_box_rows(const void* h, const float* sidecar, int C, const uint64_t* idx, int64_t m, float* out) {
@@ -374,6 +456,17 @@ int oracle_cross_filter(const void* h, const float* sidecar, int C, int op, floa
   for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
   return oracle_cross_rows(h, sidecar, C, op, idx.data(), N, out + C);
 }
+
+void oracle_weno_filter(const void* h, const float* sidecar, int C, float* out) {
+  const int64_t N = oracle_n_active(h);
+  for (int ch = 0; ch < C; ++ch) out[ch] = 0.0f;
+  std::vector<uint64_t> idx(static_cast<size_t>(N));
+  for (int64_t i = 0; i < N; ++i) idx[size_t(i)] = uint64_t(i) + 1;
+  oracle_weno_rows(h, sidecar, C, idx.data(), N, out + C);
+}
+
+// One weno5() evaluation (for the tests that pin it on closed forms).
+float oracle_weno5(float a, float b, float c, float d, float e) { return weno5(a, b, c, d, e); }
 
 void oracle_axis_filter(const void* h, const float* sidecar, int C, float* out) {
   const int64_t N = oracle_n_active(h);
