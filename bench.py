@@ -158,7 +158,8 @@ def main():
     ap.add_argument("--log2w", type=int, default=7)
     ap.add_argument("--no-extra", action="store_true", help="only the headline kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="profile mode: run only this variant (box_cs, box_c, box_s, box_p, decode, decode_sweep) and exit")
+    ap.add_argument("--only", default="", help="profile mode: run only this variant (box_cs, box_c, box_s, box_p, "
+                                               "weno_cs, decode, decode_sweep) and exit")
     ap.add_argument("--no-band", action="store_true",
                     help="skip the ~27M-voxel noisy narrow band (cached streaming box, W512, C=16; "
                          "about a minute of set-up), which is timed by default")
@@ -211,6 +212,8 @@ def main():
         variants = {"box_cs": flags_cs, "box_c": vbm.CACHED, "box_s": vbm.STREAMING, "box_p": 0}
         if args.only in ("decode", "decode_sweep"):
             fn = lambda k: vbm.decode(g, sweep=args.only == "decode_sweep")
+        elif args.only == "weno_cs":
+            fn = lambda k: vbm.weno_filter(g, scs[k], flags_cs, out=outs[k])
         else:
             fn = box_step(g, variants[args.only], scs, outs)
         ms = time_launches(fn, n_sets, args.steps, args.warmup)
@@ -281,6 +284,10 @@ def main():
                         for fl, nm in names.items():
                             t = time_launches(lambda k: vbm.axis_filter(gw, s_[k], fl, out=o_[k]), ns_, 20, 5)
                             rec("axis19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
+                        # the WENO consumer of the same 19 taps (fifth-order WENO |grad u|^2)
+                        for fl, nm in names.items():
+                            t = time_launches(lambda k: vbm.weno_filter(gw, s_[k], fl, out=o_[k]), ns_, 20, 5)
+                            rec("weno19_%s_W%d_C%d" % (nm, gw.width, ch), t, ab_w, N * ch)
             if ch != C:
                 del s_, o_
         # the pages' resolver table, on the shell that reproduces their grid (R=160, h=2:
@@ -441,6 +448,7 @@ def main():
             cpu_more["cross_sum_C%d" % ch] = oracle_rate(lambda: ref.cross(sc_c, "sum"), N * ch,
                                                          "active-voxel*channels/s")
             cpu_more["axis19_C%d" % ch] = oracle_rate(lambda: ref.axis(sc_c), N * ch, "active-voxel*channels/s")
+            cpu_more["weno19_C%d" % ch] = oracle_rate(lambda: ref.weno(sc_c), N * ch, "active-voxel*channels/s")
         # the leaf / block metadata by their plain definitions (leaves, prefix
         # directories, leafFirst, firstLeafID, jumpMap)
         cpu_more["metadata_W128"] = oracle_rate(lambda: (ref.leaves(), ref.blocks(7)), L, "leaves/s")

@@ -243,6 +243,29 @@ int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_si
 int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                     int flags, void* stream);
 
+/*
+ * WENO consumer of the 19-tap axis stencil (openvdb PR #2258, "A/B", names a
+ * 19-tap WENO consumer of the resolved taps; its arithmetic is not given there
+ * and is taken as the fifth-order WENO scheme of Jiang and Shu, J. Comput.
+ * Phys. 126 (1996), in its Hamilton-Jacobi form):
+ *   out[g*C + ch] = |grad u|^2 of channel ch at voxel g by Godunov's upwind
+ *   rule: per axis, the left- and right-biased fifth-order WENO derivatives
+ *   from the seven values u[-3..3] along that axis (unit spacing); if the
+ *   centre value is > 0, max(max(left, 0)^2, min(right, 0)^2), else
+ *   max(min(left, 0)^2, max(right, 0)^2); summed over x, y, z.
+ *   An inactive tap (index 0) reads sidecar row 0, the background value; this
+ *   consumer, unlike the summing filters, therefore reads row 0.
+ *   The fp32 evaluation order is fixed operation by operation (documented with
+ *   the kernel); no contraction, correctly rounded division, denormals kept.
+ *   flags: VBM_CACHED (the 7-direction table of the axis stencil) and
+ *   VBM_STREAMING (taps resolved as their loads are issued instead of into an
+ *   array first).  All forms give identical bits.  Row 0 of out is written as 0.
+ * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
+ * VBM_ERR_ALIAS, VBM_ERR_HIP, VBM_ERR_SIZE (as vbm_box_filter).
+ */
+int vbm_weno_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                    int flags, void* stream);
+
 /* Static English text for a status code. */
 const char* vbm_strerror(int status);
 

@@ -23,6 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     # packed-FP32 forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Rpass-analysis=kernel-resource-usage",

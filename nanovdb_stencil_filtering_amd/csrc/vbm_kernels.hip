@@ -675,20 +675,6 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
   if constexpr (kTouch) consume_touch(ahead);
 }
 
-// ---------------------------------------------------------------------------
-// device-side VBM metadata build
-// ---------------------------------------------------------------------------
-//
-// From the leaf masks in the blob, the device recomputes what the index grid
-// and the VBM derive from them (openvdb PR #2258, "What changed"; openvdb PR
-// #2263, "Built on the register-decode API"):
-//   * per leaf the 9-bit prefix directory (field k = active voxels in mask
-//     words 0..k) and leafFirst (1 + active voxels in all earlier leaves);
-//   * per block the leaf owning its first index and the jumpMap bits of the
-//     slots >= 1 whose index starts a leaf.
-// Three launches: per-leaf counts and directories, one workgroup scanning the
-// counts in place into leafFirst, one wave per block for its metadata.
-
 // The 7-direction filters with each sidecar row split over LANES = CH / 4
 // work-items (one float4 of channels each; used for CH = 16), as in
 // k_box_cached_split: the slots are decoded once into LDS (threads < W), the
@@ -752,6 +738,192 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
     reinterpret_cast<float4*>(out + idx * C + ch0)[q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
+
+// ---------------------------------------------------------------------------
+// WENO consumer on the 19 axis taps
+// ---------------------------------------------------------------------------
+//
+// openvdb PR #2258 ("A/B") times a 19-tap WENO consumer of the resolved
+// taps without giving its arithmetic.  Here it is the fifth-order WENO scheme
+// of Jiang and Shu (J. Comput. Phys. 126, 1996) in its Hamilton-Jacobi form:
+// along each axis the left- and right-biased derivatives of the field from
+// its seven values u[-3..3] (unit spacing), combined by Godunov's upwind rule
+// into |grad u|^2 per channel.  An inactive tap (index 0) reads sidecar row 0,
+// the background.  Every fp32 operation below is one IEEE rounding in the
+// order written (no contraction, correctly rounded division), which fixes the
+// result bit for bit:
+//   differences  d[j] = u[j+1] - u[j], j = 0..5
+//   left         weno5(d0, d1, d2, d3, d4), right weno5(d5, d4, d3, d2, d1)
+//   weno5(a..e)  candidates ((2a - 7b) + 11c)/6, ((-b + 5c) + 2d)/6, ((2c + 5d) - e)/6;
+//                indicators (13 q^2)/12 + (r^2)*0.25 with q, r =
+//                ((a - 2b) + c, (a - 4b) + 3c), ((b - 2c) + d, b - d),
+//                ((c - 2d) + e, (3c - 4d) + e); t = indicator + 1e-6;
+//                weights 1/(t1 t1), 6/(t2 t2), 3/(t3 t3);
+//                result ((w1 p1 + w2 p2) + w3 p3) / ((w1 + w2) + w3)
+//   Godunov      centre > 0: max(max(left, 0)^2, min(right, 0)^2), else
+//                max(min(left, 0)^2, max(right, 0)^2); axes summed (x + y) + z.
+
+__device__ __forceinline__ float weno5_derivative(float a, float b, float c, float d, float e) {
+  const float p1 = ((2.0f * a - 7.0f * b) + 11.0f * c) / 6.0f;
+  const float p2 = ((-b + 5.0f * c) + 2.0f * d) / 6.0f;
+  const float p3 = ((2.0f * c + 5.0f * d) - e) / 6.0f;
+  const float qa = (a - 2.0f * b) + c, ra = (a - 4.0f * b) + 3.0f * c;
+  const float qb = (b - 2.0f * c) + d, rb = b - d;
+  const float qc = (c - 2.0f * d) + e, rc = (3.0f * c - 4.0f * d) + e;
+  const float ta = ((13.0f * (qa * qa)) / 12.0f + (ra * ra) * 0.25f) + 1.0e-6f;
+  const float tb = ((13.0f * (qb * qb)) / 12.0f + (rb * rb) * 0.25f) + 1.0e-6f;
+  const float tc = ((13.0f * (qc * qc)) / 12.0f + (rc * rc) * 0.25f) + 1.0e-6f;
+  const float wa = 1.0f / (ta * ta), wb = 6.0f / (tb * tb), wc = 3.0f / (tc * tc);
+  return ((wa * p1 + wb * p2) + wc * p3) / ((wa + wb) + wc);
+}
+
+// |grad u|^2 contribution of one axis from its seven values u[0..6] = u[-3..3].
+__device__ __forceinline__ float weno_axis_sq(const float (&u)[7], bool outside) {
+  float d[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) d[j] = u[j + 1] - u[j];
+  const float left = weno5_derivative(d[0], d[1], d[2], d[3], d[4]);
+  const float right = weno5_derivative(d[5], d[4], d[3], d[2], d[1]);
+  const float lo = outside ? (left > 0.0f ? left : 0.0f) : (left < 0.0f ? left : 0.0f);
+  const float hi = outside ? (right < 0.0f ? right : 0.0f) : (right > 0.0f ? right : 0.0f);
+  const float l2 = lo * lo, h2 = hi * hi;
+  return l2 > h2 ? l2 : h2;
+}
+
+// Axis-stencil tap holding u[k - 3] of axis a (0 = x, 1 = y, 2 = z), k = 0..6;
+// AxisShape orders its taps x-3..x-1, y-3..y-1, z-3..z-1, centre, z+1..z+3,
+// y+1..y+3, x+1..x+3.
+__host__ __device__ constexpr int weno_tap(int a, int k) {
+  return k == 3 ? 9 : k < 3 ? 3 * a + k : (a == 2 ? 10 + (k - 4) : a == 1 ? 13 + (k - 4) : 16 + (k - 4));
+}
+
+// The WENO consumer per channel from the 19 tap values v[0..18] of one channel.
+__device__ __forceinline__ float weno_norm_sq(const float (&v)[kAxisTaps]) {
+  const bool outside = v[9] > 0.0f;
+  float sum = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    float u[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) u[k] = v[weno_tap(a, k)];
+    const float g2 = weno_axis_sq(u, outside);
+    sum = a == 0 ? g2 : sum + g2;
+  }
+  return sum;
+}
+
+// The WENO consumer kernel: one work-item per slot.  The 19 axis taps are
+// resolved by tree walks or through the staged neighbour records (CACHED),
+// either each as its value load is issued (STREAM) or all into an array first;
+// then the channels are processed four at a time (VEC: 16-byte loads and
+// stores) or one at a time, reusing the resolved taps.
+template <bool VEC, bool CACHED, bool STREAM>
+__global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
+                                              float* __restrict__ out, uint32_t C) {
+  using S = AxisShape;
+  __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  const uint32_t b = blockIdx.x;
+  if (blockIdx.x == 0)
+    for (uint32_t c = threadIdx.x; c < C; c += blockDim.x) out[c] = 0.0f;  // row 0
+  const Slot s = decode_own_slot(g, b);
+  const bool valid = s.leaf != kSentinelLeaf;
+  bool cached = false;
+  uint32_t first = 0;
+  if constexpr (CACHED) {
+    first = g.block_first_leaf[b];
+    const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
+    if (span <= kMaxCachedLeaves) {
+      stage_neighbour_records<S::kDirs>(g, first, span, staged);
+      cached = true;
+    }
+  }
+  if (!valid) return;
+  const Sidecar side = make_sidecar(sc, sc_bytes, C, 0);
+  const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+  const uint32_t j = s.leaf - first;
+  VoxelCoord p{0, 0, 0};
+  if (!cached) p = voxel_coord(g, s);
+  auto resolve = [&](int t) -> uint32_t {
+    if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t));
+    return resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t));
+  };
+  uint32_t row[S::kTaps];  // byte offset of each tap's row (index 0: row 0, the background)
+  const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
+  if constexpr (VEC) {
+    // one chunk of four channels: q-th float4 of every tap row, then the four
+    // channels one after another (fenced, so their arithmetic is not interleaved)
+    f32x4 v4[S::kTaps];
+    auto finish = [&](uint32_t q) {
+      float r[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        float v[S::kTaps];
+#pragma unroll
+        for (int t = 0; t < S::kTaps; ++t) v[t] = v4[t][c];
+        r[c] = weno_norm_sq(v);
+      }
+      reinterpret_cast<float4*>(out + idx * C)[q] = make_float4(r[0], r[1], r[2], r[3]);
+    };
+    auto load = [&](uint32_t q) {
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t)
+        v4[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, row[t] + 16 * q, 0, 0));
+    };
+    if constexpr (STREAM) {  // first chunk: each tap resolved as its load is issued
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t) {
+        row[t] = resolve(t) * side.row_bytes;
+        v4[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, row[t], 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t) row[t] = resolve(t) * side.row_bytes;
+      load(0);
+    }
+    finish(0);
+    for (uint32_t q = 1; q < C / 4; ++q) {
+      load(q);
+      finish(q);
+    }
+  } else {
+    float v[S::kTaps];
+    if constexpr (STREAM) {
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t) {
+        row[t] = resolve(t) * side.row_bytes;
+        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t], 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t) row[t] = resolve(t) * side.row_bytes;
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t)
+        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t], 0, 0));
+    }
+    out[idx * C] = weno_norm_sq(v);
+    for (uint32_t ch = 1; ch < C; ++ch) {
+#pragma unroll
+      for (int t = 0; t < S::kTaps; ++t)
+        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t] + 4 * ch, 0, 0));
+      out[idx * C + ch] = weno_norm_sq(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// device-side VBM metadata build
+// ---------------------------------------------------------------------------
+//
+// From the leaf masks in the blob, the device recomputes what the index grid
+// and the VBM derive from them (openvdb PR #2258, "What changed"; openvdb PR
+// #2263, "Built on the register-decode API"):
+//   * per leaf the 9-bit prefix directory (field k = active voxels in mask
+//     words 0..k) and leafFirst (1 + active voxels in all earlier leaves);
+//   * per block the leaf owning its first index and the jumpMap bits of the
+//     slots >= 1 whose index starts a leaf.
+// Three launches: per-leaf counts and directories, one workgroup scanning the
+// counts in place into leafFirst, one wave per block for its metadata.
 
 struct MutableGrid {
   Leaf* leaves;
@@ -1176,6 +1348,42 @@ extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const f
   }
   const DeviceGrid g = device_grid(grid, d_blob);
   launch_stencil<AxisShape, false>(g, d_sidecar, d_out, C, flags & VBM_CACHED, flags & VBM_STREAMING, st);
+  return launch_status();
+}
+
+extern "C" int vbm_weno_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
+                               int flags, void* stream) {
+  int rc = check_grid(grid, d_blob);
+  if (rc) return rc;
+  rc = check_float_buffers(grid, d_sidecar, d_out, C);
+  if (rc) return rc;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (grid->n_blocks == 0) {
+    hipLaunchKernelGGL(k_zero_index_row, dim3(1), dim3(64), 0, st, d_out, uint32_t(C));
+    return launch_status();
+  }
+  const DeviceGrid g = device_grid(grid, d_blob);
+  const uint32_t bytes = uint32_t((uint64_t(g.n_active) + 1) * uint64_t(C) * 4);
+  const bool vec = ((reinterpret_cast<uintptr_t>(d_sidecar) | reinterpret_cast<uintptr_t>(d_out)) & 15) == 0 &&
+                   C % 4 == 0;
+  const bool cached = flags & VBM_CACHED, streaming = flags & VBM_STREAMING;
+  const dim3 gd(g.n_blocks), bd(1u << g.log2w);
+  const uint32_t uc = uint32_t(C);
+#define VBM_WENO_LAUNCH(V, CA, ST) hipLaunchKernelGGL((k_weno<V, CA, ST>), gd, bd, 0, st, g, d_sidecar, bytes, d_out, uc)
+  if (vec) {
+    if (cached && streaming) VBM_WENO_LAUNCH(true, true, true);
+    else if (cached) VBM_WENO_LAUNCH(true, true, false);
+    else if (streaming) VBM_WENO_LAUNCH(true, false, true);
+    else VBM_WENO_LAUNCH(true, false, false);
+  } else {
+    if (cached && streaming) VBM_WENO_LAUNCH(false, true, true);
+    else if (cached) VBM_WENO_LAUNCH(false, true, false);
+    else if (streaming) VBM_WENO_LAUNCH(false, false, true);
+    else VBM_WENO_LAUNCH(false, false, false);
+  }
+#undef VBM_WENO_LAUNCH
   return launch_status();
 }
 

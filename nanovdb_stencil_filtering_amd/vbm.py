@@ -12,6 +12,7 @@ stream.  The names mirror the C entry points:
     box_filter(grid, sidecar, ...)     vbm_box_filter
     cross_filter(grid, sidecar, ...)   vbm_cross_filter
     axis_filter(grid, sidecar, ...)    vbm_axis_filter
+    weno_filter(grid, sidecar, ...)    vbm_weno_filter
 
 There is no CPU fallback: if the library is not built, loading raises.
 """
@@ -36,7 +37,7 @@ STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN
           -5: "VBM_ERR_RANGE", -6: "VBM_ERR_HIP", -7: "VBM_ERR_UNSUPPORTED", -8: "VBM_ERR_NOMEM"}
 
 EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_build_metadata", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
-            "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_strerror")
+            "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_weno_filter", "vbm_strerror")
 
 
 class VbmError(RuntimeError):
@@ -93,6 +94,8 @@ def load_library():
     lib.vbm_cross_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_axis_filter.restype = I
     lib.vbm_axis_filter.argtypes = [GP, P, P, P, I, I, P]
+    lib.vbm_weno_filter.restype = I
+    lib.vbm_weno_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_strerror.restype = ctypes.c_char_p
     lib.vbm_strerror.argtypes = [I]
     _lib = lib
@@ -304,4 +307,12 @@ def axis_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, 
     out, dev = _filter_out(grid, sidecar, out)
     _check(load_library().vbm_axis_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
                                           int(sidecar.shape[1]), int(flags), _stream_ptr(stream, dev)), "vbm_axis_filter")
+    return out
+
+
+def weno_filter(grid: Grid, sidecar, flags: int = CACHED | STREAMING, out=None, stream=None):
+    """vbm_weno_filter (fifth-order WENO |grad u|^2 on the 19 axis taps) -> out float32 [(N+1), C]."""
+    out, dev = _filter_out(grid, sidecar, out)
+    _check(load_library().vbm_weno_filter(ctypes.byref(grid.hdr), _blob_ptr(grid), _ptr(sidecar), _ptr(out),
+                                          int(sidecar.shape[1]), int(flags), _stream_ptr(stream, dev)), "vbm_weno_filter")
     return out

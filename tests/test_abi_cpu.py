@@ -113,8 +113,10 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
     assert lib.vbm_cross_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
     assert lib.vbm_axis_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
     assert lib.vbm_axis_filter(ctypes.byref(bad), FAKE_DEV, sc, out_far, 1, 0, None) == ARG
+    assert lib.vbm_weno_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
+    assert lib.vbm_weno_filter(ctypes.byref(bad), FAKE_DEV, sc, out_far, 1, 0, None) == ARG
     # channels, alignment, aliasing
-    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter):
+    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter, lib.vbm_weno_filter):
         assert fn(h, FAKE_DEV, sc, out_far, 0, 0, None) == ARG
         assert fn(h, FAKE_DEV, None, out_far, 1, 0, None) == ARG
         assert fn(h, FAKE_DEV, sc, None, 1, 0, None) == ARG

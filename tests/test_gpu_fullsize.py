@@ -5,7 +5,8 @@ benchmark times (no CPU fallback: every output comes from the HIP path).
   decode maps at every BlockWidth; the 27-tap box filter at C in {1, 3, 8, 16}
   (16 is the benchmark's sidecar) with all four resolver / delivery flags at
   W128 and W512; the cross sum and the 7-point Laplacian at C in {1, 8} with
-  all four flags at W64, W128, W256 and W512; the 19-tap axis filter at C=8.
+  all four flags at W64, W128, W256 and W512; the 19-tap axis filter at C=8;
+  the WENO consumer at C in {1, 4} (nonzero background row) at W128 and W512.
   Every output row is compared bit for bit with the oracle's whole-grid result
   (the oracle filters the shell in about a second).  Outputs are prefilled
   with NaN so a row the kernel skips cannot pass;
@@ -128,6 +129,21 @@ def test_cfg_shell_axis_every_row(shell):
         for flags in FLAGS:
             compare_every_row(lambda out: vbm.axis_filter(g, sct, flags, out=out), sct, want,
                               "cfg-shell axis W=%d C=8 flags=%d" % (g.width, flags))
+
+
+@pytest.mark.parametrize("C", [1, 4])
+def test_cfg_shell_weno_every_row(shell, C):
+    ref, grids = shell
+    N = grids[7].n_active
+    sc = I.sidecar(5, N, C)
+    sc[0] = 0.25  # background read by inactive taps
+    sct = torch.from_numpy(sc).cuda()
+    want = ref.weno(sc).view(np.uint32)
+    for log2w in (7, 9):
+        g = grids[log2w]
+        for flags in FLAGS:
+            compare_every_row(lambda out: vbm.weno_filter(g, sct, flags, out=out), sct, want,
+                              "cfg-shell weno W=%d C=%d flags=%d" % (g.width, C, flags))
 
 
 def test_decode_stress_full():

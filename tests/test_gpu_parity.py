@@ -148,6 +148,24 @@ def test_axis_filter(name, C):
             assert np.array_equal(u32(out), want), (log2w, flags)
 
 
+@pytest.mark.parametrize("C", [1, 3, 4, 8])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small"])
+def test_weno_filter(name, C):
+    """WENO consumer: inactive taps read row 0, so row 0 holds a nonzero background
+    here; C = 1 and 3 take the scalar kernel, 4 and 8 the float4 one."""
+    for log2w in (6, 7, 8, 9):
+        g, ref = grid_pair(name, log2w)
+        sc = I.sidecar(600 + C, g.n_active, C)
+        sc[0] = np.linspace(-0.75, 0.5, C, dtype=np.float32)
+        want = ref.weno(sc).view(np.uint32)
+        sct = torch.from_numpy(sc).cuda()
+        for flags in BOX_FLAGS:
+            say("weno %s W=%d C=%d flags=%d" % (name, 1 << log2w, C, flags))
+            out = torch.full_like(sct, float("nan"))
+            vbm.weno_filter(g, sct, flags, out=out)
+            assert np.array_equal(u32(out), want), (log2w, flags)
+
+
 def test_constant_field_interior_is_27():
     g, ref = grid_pair("dense_cube", 7)
     sc = torch.full((g.n_active + 1, 1), 0.5, dtype=torch.float32, device="cuda")
@@ -183,7 +201,7 @@ def test_filters_on_unaligned_and_wide_buffers(C):
     g, ref = grid_pair("tiny_shell", 7)
     sc = I.sidecar(400 + C, g.n_active, C)
     n = sc.size
-    want = {"box": ref.box(sc), "lap": ref.cross(sc, "laplacian"), "axis": ref.axis(sc)}
+    want = {"box": ref.box(sc), "lap": ref.cross(sc, "laplacian"), "axis": ref.axis(sc), "weno": ref.weno(sc)}
     for shift in (0, 1):  # float elements: 0 = 16-byte aligned, 1 = 4-byte aligned only
         big_in = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
         big_in[shift:] = torch.from_numpy(sc.ravel()).cuda()
@@ -195,7 +213,8 @@ def test_filters_on_unaligned_and_wide_buffers(C):
             say("unaligned/wide C=%d shift=%d flags=%d" % (C, shift, flags))
             for name, run in (("box", lambda: vbm.box_filter(g, sct, flags, out=out)),
                               ("lap", lambda: vbm.cross_filter(g, sct, flags | vbm.OP_LAPLACIAN, out=out)),
-                              ("axis", lambda: vbm.axis_filter(g, sct, flags, out=out))):
+                              ("axis", lambda: vbm.axis_filter(g, sct, flags, out=out)),
+                              ("weno", lambda: vbm.weno_filter(g, sct, flags, out=out))):
                 out.fill_(float("nan"))
                 run()
                 assert np.array_equal(u32(out), want[name].view(np.uint32)), (name, shift, flags)
@@ -263,7 +282,7 @@ def test_c_abi_refuses_pageable_host_pointers():
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     blob = ctypes.c_void_p(g.blob.data_ptr())
     dp = ctypes.c_void_p
-    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter):
+    for fn in (lib.vbm_box_filter, lib.vbm_cross_filter, lib.vbm_axis_filter, lib.vbm_weno_filter):
         assert fn(ctypes.byref(g.hdr), blob, hp, dp(dev_out.data_ptr()), C, 3, st) == -1
         assert fn(ctypes.byref(g.hdr), blob, dp(dev_sc.data_ptr()), hp, C, 3, st) == -1
     leaf = torch.zeros(g.n_slots, dtype=torch.int32, device="cuda")
@@ -289,6 +308,8 @@ def test_empty_grid_writes_row_zero():
     out = vbm.cross_filter(g, sc, vbm.OP_LAPLACIAN)
     assert torch.all(out == 0)
     out = vbm.axis_filter(g, sc)
+    assert torch.all(out == 0)
+    out = vbm.weno_filter(g, sc)
     assert torch.all(out == 0)
     leaf, off = vbm.decode_sweep(g)
     assert leaf.numel() == 0 and off.numel() == 0
