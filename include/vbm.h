@@ -33,7 +33,8 @@
  *     void*; NULL = the default stream).  Nothing synchronises.  A failed
  *     launch is reported as VBM_ERR_HIP.
  *   - Device buffers are owned by the caller.  The library allocates no device
- *     memory and keeps no state between calls.
+ *     memory and keeps no state between calls (the device-side build passes its
+ *     state from plan to fill in the caller's workspace).
  *   - Coordinates x -> di, y -> dj, z -> dk.  Leaves are 8^3; the voxel offset
  *     inside a leaf is o = (x&7)*64 + (y&7)*8 + (z&7).
  */
@@ -265,6 +266,45 @@ int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sid
  */
 int vbm_weno_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                     int flags, void* stream);
+
+/*
+ * Device-side build of the same grid from coordinates already on the GPU: the
+ * blob is byte for byte the one vbm_build writes for the same coordinates and
+ * width (openvdb PR #2258, "What changed": leaf masks and the 9-bit prefix-sum
+ * directory; openvdb PR #2263, "Built on the register-decode API": firstLeafID
+ * and the jumpMap of each block).  Three calls:
+ *
+ * vbm_build_device_workspace(n, &bytes)
+ *   Bytes of device workspace the build of n coordinates needs (about 40 B per
+ *   coordinate plus the sort's temporary storage).  Needs the GPU (the sort's
+ *   storage depends on the device).  Errors: VBM_ERR_ARG, VBM_ERR_SIZE
+ *   (n >= 2^32 - 1), VBM_ERR_HIP.
+ *
+ * vbm_build_device_plan(d_ijk, n, log2_width, d_workspace, workspace_bytes, grid, stream)
+ *   d_ijk         device int32 [n][3] coordinates, any order, duplicates allowed
+ *   d_workspace   caller-owned device memory of at least the queried bytes
+ *   grid          out: the header, including blob_bytes
+ *   Sorts the tree-order keys and counts voxels, leaves and tree nodes on
+ *   `stream`, then WAITS for the stream (the blob's size depends on the data:
+ *   this is the one entry point of the library that synchronises).  The
+ *   workspace keeps the sorted keys for vbm_build_device_fill.
+ *   Errors: VBM_ERR_ARG, VBM_ERR_SIZE (workspace too small, more than 2^32 - 2
+ *   voxels), VBM_ERR_RANGE (|coordinate| >= 2^30), VBM_ERR_UNSUPPORTED (the
+ *   bounding box of the 4096^3 root tiles holds more than 2^28 tiles),
+ *   VBM_ERR_HIP.
+ *
+ * vbm_build_device_fill(grid, n, d_workspace, workspace_bytes, d_blob, stream)
+ *   grid, n, d_workspace, workspace_bytes: as returned by / given to the plan,
+ *   with the workspace untouched since; d_blob: caller-owned device memory of
+ *   grid->blob_bytes bytes.  Writes the whole blob asynchronously on `stream`.
+ *   Errors: VBM_ERR_ARG (including a header the plan did not write),
+ *   VBM_ERR_SIZE, VBM_ERR_HIP.
+ */
+int vbm_build_device_workspace(int64_t n, uint64_t* workspace_bytes);
+int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_width, void* d_workspace,
+                          uint64_t workspace_bytes, vbm_grid* grid, void* stream);
+int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_workspace, uint64_t workspace_bytes,
+                          void* d_blob, void* stream);
 
 /* Static English text for a status code. */
 const char* vbm_strerror(int status);

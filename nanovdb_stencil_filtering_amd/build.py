@@ -1,7 +1,8 @@
 """Compile the HIP library libvbm.so for gfx950, in-tree.
 
-hipcc compiles the kernels and the C-ABI launchers (vbm_kernels.hip); g++
-compiles the host grid builder (vbm_build.cpp); hipcc links both into
+hipcc compiles the kernels and the C-ABI launchers (vbm_kernels.hip) and the
+device-side grid build (vbm_build_device.hip) in parallel; g++ compiles the
+host grid builder (vbm_build.cpp); hipcc links them into
 nanovdb_stencil_filtering_amd/_lib/libvbm.so.  Kernel resource usage (VGPRs,
 SGPRs, scratch, LDS, occupancy) is written to _lib/resource_usage.txt.
 """
@@ -29,7 +30,7 @@ HIP_FLAGS = [
     "-Rpass-analysis=kernel-resource-usage",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
-CXX_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I" + INCLUDE]
+CXX_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I" + INCLUDE, "-I" + CSRC]
 
 
 def _run(cmd, log=None):
@@ -43,15 +44,36 @@ def _run(cmd, log=None):
     return r.stdout
 
 
+def _start(cmd, log):
+    f = open(log, "w")
+    return subprocess.Popen(cmd, stdout=f, stderr=subprocess.STDOUT, text=True), f, cmd, log
+
+
+def _finish(job):
+    proc, f, cmd, log = job
+    rc = proc.wait()
+    f.close()
+    if rc != 0:
+        with open(log) as fh:
+            sys.stderr.write(fh.read()[-20000:])
+        raise RuntimeError("command failed: " + " ".join(cmd))
+
+
 def build() -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     k_obj = os.path.join(LIBDIR, "vbm_kernels.o")
+    d_obj = os.path.join(LIBDIR, "vbm_build_device.o")
     b_obj = os.path.join(LIBDIR, "vbm_build.o")
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_kernels.hip"), "-o", k_obj],
-         log=os.path.join(LIBDIR, "resource_usage.txt"))
+    # the two HIP sources compile in parallel
+    jobs = [_start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_kernels.hip"), "-o", k_obj],
+                   os.path.join(LIBDIR, "resource_usage.txt")),
+            _start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_build_device.hip"), "-o", d_obj],
+                   os.path.join(LIBDIR, "resource_usage_build_device.txt"))]
     _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "vbm_build.cpp"), "-o", b_obj])
+    for j in jobs:
+        _finish(j)
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, b_obj, "-o", tmp])
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, d_obj, b_obj, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

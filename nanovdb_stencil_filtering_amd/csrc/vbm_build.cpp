@@ -28,15 +28,13 @@
 #include <vector>
 
 #include "vbm.h"
+#include "vbm_layout.hpp"
 
 namespace {
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
-constexpr uint64_t kAlign = 256;
 constexpr int64_t kCoordLimit = int64_t(1) << 30;
-constexpr uint64_t kMaxActive = 0xFFFFFFFEull;
-
-uint64_t align_up(uint64_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+constexpr uint64_t kMaxActive = vbm_layout::kMaxActive;
 
 struct RootKey {
   int32_t x, y, z;
@@ -186,23 +184,8 @@ extern "C" int vbm_build(const int32_t* ijk, int64_t n, int log2_width, vbm_grid
 
     // ---- serialise ------------------------------------------------------------
     vbm_grid g;
-    std::memset(&g, 0, sizeof(g));
-    g.magic = VBM_GRID_MAGIC;
-    g.log2_width = log2_width;
-    g.n_active = N;
-    g.n_leaves = uint32_t(L);
-    g.n_blocks = uint32_t(nb);
-    g.n_root = uint32_t(n_root);
-    g.n_upper = uint32_t(n_root);
-    g.n_lower = uint32_t(n_lower);
-    uint64_t off = 0;
-    g.off_leaves = off;            off = align_up(off + L * sizeof(LeafRecord));
-    g.off_root = off;              off = align_up(off + n_root * sizeof(RootTileRecord));
-    g.off_upper = off;             off = align_up(off + upper.size() * 4);
-    g.off_lower = off;             off = align_up(off + lower.size() * 4);
-    g.off_block_first_leaf = off;  off = align_up(off + nb * 4);
-    g.off_block_jump = off;        off = align_up(off + nb * words * 8);
-    g.blob_bytes = off > 0 ? off : kAlign;
+    const int rc = vbm_layout::layout(N, L, n_root, n_lower, log2_width, &g);
+    if (rc != VBM_OK) return rc;
 
     uint8_t* blob = static_cast<uint8_t*>(std::calloc(1, g.blob_bytes));
     if (!blob) return VBM_ERR_NOMEM;

@@ -1,0 +1,482 @@
+// Device-side build of the index grid and its VoxelBlockManager metadata from
+// a set of coordinates already on the GPU (the same blob, byte for byte, as
+// the host builder in vbm_build.cpp).
+//
+// The blob is what every stage of the pipeline reads: per leaf the 512-bit
+// value mask, the 9-bit prefix-sum directory and the first index (openvdb PR
+// #2258, "What changed"), the tree the resolvers walk (openvdb PR #2263,
+// "Summary"), and per block firstLeafID and the jumpMap (openvdb PR #2263,
+// "Built on the register-decode API": the first leaf, spanned leaves =
+// 1 + popcount(jumpMap)).
+//
+// Plan (vbm_build_device_plan), on the caller's stream and workspace:
+//   1. bounding box of the root tiles (x >> 12, ...) and the range check;
+//   2. one 64-bit key per coordinate: the root tile's position in that box,
+//      linearised x-major (so keys order root tiles lexicographically, as the
+//      host's dense root ranks do), above the 36-bit position in the tile
+//      (upper slot, lower slot, voxel offset, each x-major) -- tree order;
+//   3. radix sort of the keys over the bits in use, then duplicates removed;
+//   4. counts of voxels, leaves (key >> 9), lower nodes (key >> 21) and root
+//      tiles (key >> 36), read back by the host, which lays out the blob.
+// Fill (vbm_build_device_fill), asynchronous:
+//   leaf ids, lower-node ids and root ranks by scans over start flags; leaf
+//   masks by atomic OR of each voxel's bit; one work-item per leaf writes its
+//   record (prefix directory from the mask) and its entries in the lower, upper
+//   and root sections; the block metadata by scatter: each leaf sets the jumpMap
+//   bit of its first index and writes firstLeafID of every block whose first
+//   index it holds (no search).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_scan.hpp>
+#include <rocprim/device/device_select.hpp>
+#include <rocprim/iterator/counting_iterator.hpp>
+#include <rocprim/iterator/transform_iterator.hpp>
+
+#include "vbm.h"
+#include "vbm_host_checks.hpp"
+#include "vbm_layout.hpp"
+
+namespace {
+
+constexpr int32_t kCoordLimit = int32_t(1) << 30;
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+
+// First 256 bytes of the workspace.
+struct BuildHeader {
+  int32_t lo[3];         // root-tile bounding box (inclusive), x >> 12 etc.
+  int32_t hi[3];
+  uint32_t status;       // bit 0: a coordinate with |c| >= 2^30
+  uint32_t pad;
+  uint64_t n_unique;     // N after removing duplicates
+  unsigned long long n_leaves, n_lower, n_root;
+};
+static_assert(sizeof(BuildHeader) <= 256, "workspace header");
+
+// Workspace sections for n coordinates (256-byte aligned offsets).
+struct WorkspaceLayout {
+  uint64_t keys_a, keys_b, leaf_of_voxel, leaf_key, leaf_first, lower_id, root_rank, temp, temp_bytes, total;
+};
+
+WorkspaceLayout workspace_layout(uint64_t n, uint64_t temp_bytes) {
+  using vbm_layout::align_up;
+  WorkspaceLayout w;
+  uint64_t off = 256;
+  w.keys_a = off;        off = align_up(off + 8 * n);
+  w.keys_b = off;        off = align_up(off + 8 * n);
+  w.leaf_of_voxel = off; off = align_up(off + 4 * n);
+  w.leaf_key = off;      off = align_up(off + 8 * n);
+  w.leaf_first = off;    off = align_up(off + 4 * n);
+  w.lower_id = off;      off = align_up(off + 4 * n);
+  w.root_rank = off;     off = align_up(off + 4 * n);
+  w.temp = off;          off = align_up(off + temp_bytes);
+  w.temp_bytes = temp_bytes;
+  w.total = off;
+  return w;
+}
+
+// Start flags over sorted keys: element i starts a new group of key >> shift.
+struct KeyGroupStart {
+  const uint64_t* keys;
+  uint32_t shift;
+  __host__ __device__ uint32_t operator()(uint64_t i) const {
+    return i == 0 || (keys[i] >> shift) != (keys[i - 1] >> shift) ? 1u : 0u;
+  }
+};
+
+using Counting = rocprim::counting_iterator<uint64_t>;
+using StartFlags = rocprim::transform_iterator<Counting, KeyGroupStart, uint32_t>;
+
+// Largest temporary storage the plan and fill ask rocPRIM for, for n keys.
+hipError_t temp_storage_bytes(uint64_t n, hipStream_t st, uint64_t* bytes) {
+  size_t sort = 0, uniq = 0, scan = 0;
+  uint64_t* k = nullptr;
+  uint64_t* cnt = nullptr;
+  uint32_t* out = nullptr;
+  hipError_t e = rocprim::radix_sort_keys(nullptr, sort, k, k, n, 0, 64, st);
+  if (e != hipSuccess) return e;
+  e = rocprim::unique(nullptr, uniq, k, k, cnt, n, rocprim::equal_to<uint64_t>(), st);
+  if (e != hipSuccess) return e;
+  StartFlags flags(Counting(0), KeyGroupStart{k, 9});
+  e = rocprim::inclusive_scan(nullptr, scan, flags, out, n, rocprim::plus<uint32_t>(), st);
+  if (e != hipSuccess) return e;
+  size_t m = sort > uniq ? sort : uniq;
+  *bytes = m > scan ? m : scan;
+  return hipSuccess;
+}
+
+__global__ void k_build_init(BuildHeader* h) {
+  if (threadIdx.x == 0) {
+    for (int a = 0; a < 3; ++a) {
+      h->lo[a] = INT32_MAX;
+      h->hi[a] = INT32_MIN;
+    }
+    h->status = 0;
+    h->n_unique = 0;
+    h->n_leaves = h->n_lower = h->n_root = 0;
+  }
+}
+
+__device__ __forceinline__ int32_t wave_min(int32_t v) {
+  for (int d = 32; d > 0; d >>= 1) v = min(v, __shfl_xor(v, d));
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+  for (int d = 32; d > 0; d >>= 1) v = max(v, __shfl_xor(v, d));
+  return v;
+}
+
+// Root-tile bounding box and the coordinate range check.
+__global__ void __launch_bounds__(256) k_build_bounds(const int32_t* __restrict__ ijk, uint64_t n, BuildHeader* h) {
+  int32_t lo[3] = {INT32_MAX, INT32_MAX, INT32_MAX}, hi[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
+  bool bad = false;
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const int32_t c = ijk[3 * i + a];
+      bad |= c <= -kCoordLimit || c >= kCoordLimit;
+      lo[a] = min(lo[a], c >> 12);
+      hi[a] = max(hi[a], c >> 12);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    lo[a] = wave_min(lo[a]);
+    hi[a] = wave_max(hi[a]);
+  }
+  const bool any_bad = __any(bad);
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      atomicMin(&h->lo[a], lo[a]);
+      atomicMax(&h->hi[a], hi[a]);
+    }
+    if (any_bad) atomicOr(&h->status, 1u);
+  }
+}
+
+// Position of a voxel inside its root tile, in tree order: upper slot, lower
+// slot, voxel offset, each x-major (bits 35..0).
+__device__ __forceinline__ uint64_t in_tile_position(int32_t x, int32_t y, int32_t z) {
+  const uint64_t ux = (uint32_t(x) >> 7) & 31, uy = (uint32_t(y) >> 7) & 31, uz = (uint32_t(z) >> 7) & 31;
+  const uint64_t lx = (uint32_t(x) >> 3) & 15, ly = (uint32_t(y) >> 3) & 15, lz = (uint32_t(z) >> 3) & 15;
+  const uint64_t vx = uint32_t(x) & 7, vy = uint32_t(y) & 7, vz = uint32_t(z) & 7;
+  return (ux << 31) | (uy << 26) | (uz << 21) | (lx << 17) | (ly << 13) | (lz << 9) | (vx << 6) | (vy << 3) | vz;
+}
+
+struct TileBox {
+  int32_t lo[3];
+  uint64_t span_y, span_z;  // tiles along y and z
+};
+
+__device__ __forceinline__ TileBox tile_box(const BuildHeader* h) {
+  TileBox b;
+  for (int a = 0; a < 3; ++a) b.lo[a] = h->lo[a];
+  b.span_y = uint64_t(int64_t(h->hi[1]) - h->lo[1] + 1);
+  b.span_z = uint64_t(int64_t(h->hi[2]) - h->lo[2] + 1);
+  return b;
+}
+
+__global__ void __launch_bounds__(256) k_build_keys(const int32_t* __restrict__ ijk, uint64_t n, const BuildHeader* h,
+                                                    uint64_t* __restrict__ keys) {
+  const TileBox box = tile_box(h);
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x) {
+    const int32_t x = ijk[3 * i], y = ijk[3 * i + 1], z = ijk[3 * i + 2];
+    const uint64_t tile = (uint64_t(int64_t(x >> 12) - box.lo[0]) * box.span_y + uint64_t(int64_t(y >> 12) - box.lo[1])) *
+                              box.span_z +
+                          uint64_t(int64_t(z >> 12) - box.lo[2]);
+    keys[i] = (tile << 36) | in_tile_position(x, y, z);
+  }
+}
+
+// Counts of leaves, lower nodes and root tiles among the N sorted unique keys.
+__global__ void __launch_bounds__(256) k_build_counts(const uint64_t* __restrict__ keys, BuildHeader* h) {
+  const uint64_t N = h->n_unique;
+  uint32_t leaves = 0, lowers = 0, roots = 0;
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < N; i += uint64_t(gridDim.x) * blockDim.x) {
+    const uint64_t k = keys[i], p = i ? keys[i - 1] : ~k;
+    leaves += (k >> 9) != (p >> 9);
+    lowers += (k >> 21) != (p >> 21);
+    roots += (k >> 36) != (p >> 36);
+  }
+  for (int d = 32; d > 0; d >>= 1) {
+    leaves += __shfl_xor(leaves, d);
+    lowers += __shfl_xor(lowers, d);
+    roots += __shfl_xor(roots, d);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&h->n_leaves, (unsigned long long)leaves);
+    atomicAdd(&h->n_lower, (unsigned long long)lowers);
+    atomicAdd(&h->n_root, (unsigned long long)roots);
+  }
+}
+
+// Blob initialisation: zero everywhere except the upper and lower node
+// sections, whose entries start as kNone (no child).  16-byte stores.
+__global__ void __launch_bounds__(256) k_fill_init(uint4* __restrict__ blob, uint64_t pieces, uint64_t none_a0,
+                                                   uint64_t none_a1, uint64_t none_b0, uint64_t none_b1) {
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < pieces; i += uint64_t(gridDim.x) * blockDim.x) {
+    const bool none = (i >= none_a0 && i < none_a1) || (i >= none_b0 && i < none_b1);
+    blob[i] = none ? make_uint4(kNone, kNone, kNone, kNone) : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Record of each leaf start: its key >> 9 and the index of its first voxel.
+// (Every id below is checked against the header's counts, so a header that
+// does not belong to the workspace can give a wrong blob but no access outside
+// the buffers.)
+__global__ void __launch_bounds__(256) k_fill_leaf_starts(const uint64_t* __restrict__ keys, uint64_t N, uint64_t L,
+                                                          const uint32_t* __restrict__ leaf_of_voxel,
+                                                          uint64_t* __restrict__ leaf_key,
+                                                          uint32_t* __restrict__ leaf_first) {
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < N; i += uint64_t(gridDim.x) * blockDim.x) {
+    if (i == 0 || (keys[i] >> 9) != (keys[i - 1] >> 9)) {
+      const uint32_t l = leaf_of_voxel[i] - 1;  // inclusive count of starts
+      if (l >= L) continue;
+      leaf_key[l] = keys[i] >> 9;
+      leaf_first[l] = uint32_t(i + 1);
+    }
+  }
+}
+
+struct BlobLeaf {  // the 128-byte leaf record of include/vbm.h
+  uint64_t mask[8];
+  uint64_t prefix;
+  uint64_t first;
+  int32_t origin[3];
+  uint32_t lower;
+  uint32_t upper;
+  uint32_t pad[7];
+};
+static_assert(sizeof(BlobLeaf) == 128, "leaf record");
+
+// Each voxel sets its bit in its leaf's value mask.
+__global__ void __launch_bounds__(256) k_fill_masks(const uint64_t* __restrict__ keys, uint64_t N, uint64_t L,
+                                                    const uint32_t* __restrict__ leaf_of_voxel, BlobLeaf* leaves) {
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < N; i += uint64_t(gridDim.x) * blockDim.x) {
+    const uint32_t o = uint32_t(keys[i] & 511);
+    const uint32_t l = leaf_of_voxel[i] - 1;
+    if (l >= L) continue;
+    atomicOr(reinterpret_cast<unsigned long long*>(&leaves[l].mask[o >> 6]),
+             (unsigned long long)1 << (o & 63));
+  }
+}
+
+struct BlobSections {
+  BlobLeaf* leaves;
+  int32_t* root;       // 4 ints per tile: key x, y, z, upper node
+  uint32_t* upper;     // n_root * 32768
+  uint32_t* lower;     // n_lower * 4096
+  uint32_t n_root, n_lower;
+};
+
+// One work-item per leaf: prefix directory, first index, origin, parents; the
+// leaf's entry in its lower node, and (for the first leaf of a lower node /
+// root tile) the entries of the upper node and the root table.
+__global__ void __launch_bounds__(256) k_fill_leaves(uint64_t L, const uint64_t* __restrict__ leaf_key,
+                                                     const uint32_t* __restrict__ leaf_first,
+                                                     const uint32_t* __restrict__ lower_id,
+                                                     const uint32_t* __restrict__ root_rank, const BuildHeader* h,
+                                                     BlobSections blob) {
+  const TileBox box = tile_box(h);
+  for (uint64_t l = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; l < L; l += uint64_t(gridDim.x) * blockDim.x) {
+    BlobLeaf& rec = blob.leaves[l];
+    uint64_t count = 0, dir = 0;
+#pragma unroll
+    for (int w = 0; w < 7; ++w) {
+      count += __popcll(rec.mask[w]);
+      dir |= count << (9 * w);
+    }
+    const uint64_t lk = leaf_key[l];
+    const uint64_t tile = lk >> 27;  // position of the root tile in the bounding box
+    const int32_t rx = box.lo[0] + int32_t(tile / (box.span_y * box.span_z));
+    const int32_t ry = box.lo[1] + int32_t((tile / box.span_z) % box.span_y);
+    const int32_t rz = box.lo[2] + int32_t(tile % box.span_z);
+    const uint32_t t = uint32_t(lk & ((uint64_t(1) << 27) - 1));  // upper slot (15 bits) | lower slot (12 bits)
+    const uint32_t low = lower_id[l] - 1, up = root_rank[l] - 1;
+    if (low >= blob.n_lower || up >= blob.n_root) continue;
+    rec.prefix = dir;
+    rec.first = leaf_first[l];
+    rec.origin[0] = rx * 4096 + int32_t((t >> 22) & 31) * 128 + int32_t((t >> 8) & 15) * 8;
+    rec.origin[1] = ry * 4096 + int32_t((t >> 17) & 31) * 128 + int32_t((t >> 4) & 15) * 8;
+    rec.origin[2] = rz * 4096 + int32_t((t >> 12) & 31) * 128 + int32_t(t & 15) * 8;
+    rec.lower = low;
+    rec.upper = up;
+    blob.lower[uint64_t(low) * 4096 + (t & 4095)] = uint32_t(l);
+    const uint64_t plk = l ? leaf_key[l - 1] : ~lk;
+    if ((lk >> 12) != (plk >> 12)) blob.upper[uint64_t(up) * 32768 + (t >> 12)] = low;
+    if ((lk >> 27) != (plk >> 27)) {
+      int32_t* r = blob.root + 4 * uint64_t(up);
+      r[0] = rx;
+      r[1] = ry;
+      r[2] = rz;
+      r[3] = int32_t(up);
+    }
+  }
+}
+
+// Block metadata by scatter: leaf l (first index f, c voxels) sets the jumpMap
+// bit of slot (f - 1) % W of block (f - 1) / W unless it starts the block, and
+// is firstLeafID of every block whose first index 1 + bW lies in [f, f + c).
+__global__ void __launch_bounds__(256) k_fill_blocks(uint64_t L, uint64_t N, int log2w,
+                                                     const uint32_t* __restrict__ leaf_first,
+                                                     uint32_t* __restrict__ block_first_leaf,
+                                                     uint64_t* block_jump) {
+  const uint64_t W = uint64_t(1) << log2w, words = W / 64;
+  for (uint64_t l = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; l < L; l += uint64_t(gridDim.x) * blockDim.x) {
+    const uint64_t f = leaf_first[l];
+    const uint64_t end = l + 1 < L ? uint64_t(leaf_first[l + 1]) : N + 1;  // one past the leaf's last index
+    const uint64_t s = (f - 1) & (W - 1), b = (f - 1) >> log2w;
+    if (s != 0)
+      atomicOr(reinterpret_cast<unsigned long long*>(&block_jump[b * words + s / 64]),
+               (unsigned long long)1 << (s % 64));
+    for (uint64_t bb = (f - 1 + W - 1) >> log2w; 1 + (bb << log2w) < end; ++bb) block_first_leaf[bb] = uint32_t(l);
+  }
+}
+
+uint32_t grid_for(uint64_t items) {
+  const uint64_t g = (items + 255) / 256;
+  return uint32_t(g < 1 ? 1 : (g > 8192 ? 8192 : g));
+}
+
+// Runs a rocPRIM call f(temp, bytes) after checking, with a size query
+// f(nullptr, bytes), that its temporary storage fits the workspace's.
+template <class F>
+int run_with_temp(void* temp, uint64_t temp_bytes, F&& f) {
+  size_t need = 0;
+  if (f(nullptr, need) != hipSuccess) return VBM_ERR_HIP;
+  if (need > temp_bytes) return VBM_ERR_SIZE;
+  size_t have = size_t(temp_bytes);
+  return f(temp, have) == hipSuccess ? VBM_OK : VBM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int vbm_build_device_workspace(int64_t n, uint64_t* workspace_bytes) {
+  if (!workspace_bytes || n < 0) return VBM_ERR_ARG;
+  if (uint64_t(n) >= 0xFFFFFFFFull) return VBM_ERR_SIZE;
+  uint64_t temp = 0;
+  if (temp_storage_bytes(uint64_t(n), nullptr, &temp) != hipSuccess) {
+    (void)hipGetLastError();
+    return VBM_ERR_HIP;
+  }
+  *workspace_bytes = workspace_layout(uint64_t(n), temp).total;
+  return VBM_OK;
+}
+
+extern "C" int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_width, void* d_workspace,
+                                     uint64_t workspace_bytes, vbm_grid* grid, void* stream) {
+  if (!grid || !d_workspace || n < 0 || (n > 0 && !d_ijk)) return VBM_ERR_ARG;
+  if (log2_width < 6 || log2_width > 9) return VBM_ERR_ARG;
+  if (uint64_t(n) >= 0xFFFFFFFFull) return VBM_ERR_SIZE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint64_t temp = 0;
+  if (temp_storage_bytes(uint64_t(n), st, &temp) != hipSuccess) {
+    (void)hipGetLastError();
+    return VBM_ERR_HIP;
+  }
+  const WorkspaceLayout w = workspace_layout(uint64_t(n), temp);
+  if (workspace_bytes < w.total) return VBM_ERR_SIZE;
+  int rc = n > 0 ? vbm_host::check_kernel_memory({d_ijk, d_workspace}) : vbm_host::check_kernel_memory({d_workspace});
+  if (rc) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+  BuildHeader* h = reinterpret_cast<BuildHeader*>(ws);
+  uint64_t* keys_a = reinterpret_cast<uint64_t*>(ws + w.keys_a);
+  uint64_t* keys_b = reinterpret_cast<uint64_t*>(ws + w.keys_b);
+  hipLaunchKernelGGL(k_build_init, dim3(1), dim3(64), 0, st, h);
+  if (n > 0) hipLaunchKernelGGL(k_build_bounds, dim3(grid_for(uint64_t(n))), dim3(256), 0, st, d_ijk, uint64_t(n), h);
+  BuildHeader host;
+  if (hipMemcpyAsync(&host, h, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return VBM_ERR_HIP;
+  if (host.status & 1u) return VBM_ERR_RANGE;
+  unsigned key_bits = 36;
+  if (n > 0) {
+    const uint64_t tiles = uint64_t(int64_t(host.hi[0]) - host.lo[0] + 1) * uint64_t(int64_t(host.hi[1]) - host.lo[1] + 1) *
+                           uint64_t(int64_t(host.hi[2]) - host.lo[2] + 1);
+    unsigned tile_bits = 0;
+    while (tile_bits < 64 && (uint64_t(1) << tile_bits) < tiles) ++tile_bits;
+    if (tile_bits > 28) return VBM_ERR_UNSUPPORTED;  // the key keeps 28 bits for the root tile
+    key_bits += tile_bits;
+    hipLaunchKernelGGL(k_build_keys, dim3(grid_for(uint64_t(n))), dim3(256), 0, st, d_ijk, uint64_t(n), h, keys_a);
+    void* temp = ws + w.temp;
+    const uint64_t nn = uint64_t(n);
+    if ((rc = run_with_temp(temp, w.temp_bytes, [&](void* t, size_t& b) {
+           return rocprim::radix_sort_keys(t, b, keys_a, keys_b, nn, 0, key_bits, st);
+         })))
+      return rc;
+    if ((rc = run_with_temp(temp, w.temp_bytes, [&](void* t, size_t& b) {
+           return rocprim::unique(t, b, keys_b, keys_a, &h->n_unique, nn, rocprim::equal_to<uint64_t>(), st);
+         })))
+      return rc;
+    hipLaunchKernelGGL(k_build_counts, dim3(grid_for(uint64_t(n))), dim3(256), 0, st, keys_a, h);
+    if (hipMemcpyAsync(&host, h, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return VBM_ERR_HIP;
+  }
+  if ((rc = vbm_host::launch_status())) return rc;
+  return vbm_layout::layout(host.n_unique, host.n_leaves, host.n_root, host.n_lower, log2_width, grid);
+}
+
+extern "C" int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_workspace, uint64_t workspace_bytes,
+                                     void* d_blob, void* stream) {
+  if (!grid || grid->magic != VBM_GRID_MAGIC || !d_workspace || !d_blob || n < 0) return VBM_ERR_ARG;
+  if (grid->log2_width < 6 || grid->log2_width > 9 || grid->n_active > uint64_t(n) || grid->n_leaves > grid->n_active)
+    return VBM_ERR_ARG;
+  if (uint64_t(n) >= 0xFFFFFFFFull) return VBM_ERR_SIZE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint64_t temp = 0;
+  if (temp_storage_bytes(uint64_t(n), st, &temp) != hipSuccess) {
+    (void)hipGetLastError();
+    return VBM_ERR_HIP;
+  }
+  const WorkspaceLayout w = workspace_layout(uint64_t(n), temp);
+  if (workspace_bytes < w.total) return VBM_ERR_SIZE;
+  vbm_grid check;
+  if (vbm_layout::layout(grid->n_active, grid->n_leaves, grid->n_root, grid->n_lower, grid->log2_width, &check) ||
+      std::memcmp(&check, grid, sizeof(check)) != 0)
+    return VBM_ERR_ARG;  // not a header that vbm_build_device_plan wrote
+  int rc = vbm_host::check_kernel_memory({d_workspace, d_blob});
+  if (rc) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+  uint8_t* blob = static_cast<uint8_t*>(d_blob);
+  const BuildHeader* h = reinterpret_cast<const BuildHeader*>(ws);
+  const uint64_t* keys = reinterpret_cast<const uint64_t*>(ws + w.keys_a);
+  uint32_t* leaf_of_voxel = reinterpret_cast<uint32_t*>(ws + w.leaf_of_voxel);
+  uint64_t* leaf_key = reinterpret_cast<uint64_t*>(ws + w.leaf_key);
+  uint32_t* leaf_first = reinterpret_cast<uint32_t*>(ws + w.leaf_first);
+  uint32_t* lower_id = reinterpret_cast<uint32_t*>(ws + w.lower_id);
+  uint32_t* root_rank = reinterpret_cast<uint32_t*>(ws + w.root_rank);
+  const uint64_t N = grid->n_active, L = grid->n_leaves;
+  const uint64_t pieces = grid->blob_bytes / 16;
+  hipLaunchKernelGGL(k_fill_init, dim3(grid_for(pieces)), dim3(256), 0, st, reinterpret_cast<uint4*>(blob), pieces,
+                     grid->off_upper / 16, (grid->off_upper + uint64_t(grid->n_upper) * 32768 * 4) / 16,
+                     grid->off_lower / 16, (grid->off_lower + uint64_t(grid->n_lower) * 4096 * 4) / 16);
+  if (N > 0) {
+    void* temp = ws + w.temp;
+    // inclusive scans of start flags: leaf of each voxel, lower node and root rank of each leaf
+    auto scan = [&](const uint64_t* k, uint32_t shift, uint32_t* out, uint64_t count) {
+      return run_with_temp(temp, w.temp_bytes, [&](void* t, size_t& b) {
+        return rocprim::inclusive_scan(t, b, StartFlags(Counting(0), KeyGroupStart{k, shift}), out, count,
+                                       rocprim::plus<uint32_t>(), st);
+      });
+    };
+    if ((rc = scan(keys, 9, leaf_of_voxel, N))) return rc;
+    hipLaunchKernelGGL(k_fill_leaf_starts, dim3(grid_for(N)), dim3(256), 0, st, keys, N, L, leaf_of_voxel, leaf_key,
+                       leaf_first);
+    if ((rc = scan(leaf_key, 12, lower_id, L))) return rc;
+    if ((rc = scan(leaf_key, 27, root_rank, L))) return rc;
+    BlobLeaf* leaves = reinterpret_cast<BlobLeaf*>(blob + grid->off_leaves);
+    hipLaunchKernelGGL(k_fill_masks, dim3(grid_for(N)), dim3(256), 0, st, keys, N, L, leaf_of_voxel, leaves);
+    BlobSections sec{leaves, reinterpret_cast<int32_t*>(blob + grid->off_root),
+                     reinterpret_cast<uint32_t*>(blob + grid->off_upper),
+                     reinterpret_cast<uint32_t*>(blob + grid->off_lower), grid->n_root, grid->n_lower};
+    hipLaunchKernelGGL(k_fill_leaves, dim3(grid_for(L)), dim3(256), 0, st, L, leaf_key, leaf_first, lower_id,
+                       root_rank, h, sec);
+    hipLaunchKernelGGL(k_fill_blocks, dim3(grid_for(L)), dim3(256), 0, st, L, N, grid->log2_width, leaf_first,
+                       reinterpret_cast<uint32_t*>(blob + grid->off_block_first_leaf),
+                       reinterpret_cast<uint64_t*>(blob + grid->off_block_jump));
+  }
+  return vbm_host::launch_status();
+}

@@ -22,6 +22,7 @@
 
 #include "vbm.h"
 #include "vbm_device.hpp"
+#include "vbm_host_checks.hpp"
 
 using namespace vbm;
 
@@ -1080,24 +1081,8 @@ DeviceGrid device_grid(const vbm_grid* grid, const void* d_blob) {
   return g;
 }
 
-int launch_status() { return hipGetLastError() == hipSuccess ? VBM_OK : VBM_ERR_HIP; }
-
-// Every pointer a kernel dereferences must be memory the GPU can reach: device
-// memory, pinned host memory or managed memory.  A pageable host pointer, or
-// an address HIP does not know, would fault the GPU, so it is refused before
-// any launch.
-int check_kernel_memory(std::initializer_list<const void*> ptrs) {
-  for (const void* p : ptrs) {
-    hipPointerAttribute_t a;
-    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-      (void)hipGetLastError();  // the failed query must not surface as a later launch error
-      return VBM_ERR_ARG;
-    }
-    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeHost && a.type != hipMemoryTypeManaged)
-      return VBM_ERR_ARG;
-  }
-  return VBM_OK;
-}
+using vbm_host::check_kernel_memory;
+using vbm_host::launch_status;
 
 int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out, int C) {
   if (!sc || !out || C < 1) return VBM_ERR_ARG;

@@ -5,6 +5,7 @@ kernels behind the C ABI.  PyTorch provides device memory and the current
 stream.  The names mirror the C entry points:
 
     build(coords, log2_width)          vbm_build  (host) + copy of the blob to the GPU
+    build_device(coords, log2_width)   vbm_build_device_workspace / _plan / _fill (on the GPU)
     build_metadata(grid)               vbm_build_metadata (device-side leaf/block metadata)
     decode(grid)                       vbm_decode
     decode_sweep(grid)                 vbm_decode_sweep
@@ -37,7 +38,8 @@ STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN
           -5: "VBM_ERR_RANGE", -6: "VBM_ERR_HIP", -7: "VBM_ERR_UNSUPPORTED", -8: "VBM_ERR_NOMEM"}
 
 EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_build_metadata", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
-            "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_weno_filter", "vbm_strerror")
+            "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_weno_filter",
+            "vbm_build_device_workspace", "vbm_build_device_plan", "vbm_build_device_fill", "vbm_strerror")
 
 
 class VbmError(RuntimeError):
@@ -94,6 +96,12 @@ def load_library():
     lib.vbm_cross_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_axis_filter.restype = I
     lib.vbm_axis_filter.argtypes = [GP, P, P, P, I, I, P]
+    lib.vbm_build_device_workspace.restype = I
+    lib.vbm_build_device_workspace.argtypes = [I64, ctypes.POINTER(ctypes.c_uint64)]
+    lib.vbm_build_device_plan.restype = I
+    lib.vbm_build_device_plan.argtypes = [P, I64, I, P, ctypes.c_uint64, GP, P]
+    lib.vbm_build_device_fill.restype = I
+    lib.vbm_build_device_fill.argtypes = [GP, I64, P, ctypes.c_uint64, P, P]
     lib.vbm_weno_filter.restype = I
     lib.vbm_weno_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_strerror.restype = ctypes.c_char_p
@@ -194,6 +202,32 @@ def build(coords: np.ndarray, log2_width: int, device="cuda") -> Grid:
     import torch
     hdr, host = build_host(coords, log2_width)
     blob = torch.from_numpy(host).to(device)
+    return Grid(hdr, blob)
+
+
+def build_device(coords, log2_width: int, device="cuda", stream=None) -> Grid:
+    """vbm_build_device_*: build the grid on the GPU from coordinates (a torch int32
+    [n, 3] tensor on the device, or anything numpy converts; copied to `device`).
+    The workspace is a torch allocation released on return; the plan waits for the
+    stream once (the blob's size depends on the data)."""
+    import torch
+    lib = load_library()
+    c = coords if isinstance(coords, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(coords, np.int32))
+    c = c.to(device=device, dtype=torch.int32).reshape(-1, 3).contiguous()
+    dev = c.device
+    if dev.type != "cuda":
+        raise ValueError("build_device needs a GPU device, not %s" % dev)
+    n = int(c.shape[0])
+    need = ctypes.c_uint64()
+    _check(lib.vbm_build_device_workspace(n, ctypes.byref(need)), "vbm_build_device_workspace")
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    hdr = GridHeader()
+    sp = _stream_ptr(stream, dev)
+    _check(lib.vbm_build_device_plan(_ptr(c), n, int(log2_width), _ptr(ws), need.value, ctypes.byref(hdr), sp),
+           "vbm_build_device_plan")
+    blob = torch.empty(int(hdr.blob_bytes), dtype=torch.uint8, device=dev)
+    _check(lib.vbm_build_device_fill(ctypes.byref(hdr), n, _ptr(ws), need.value, _ptr(blob), sp),
+           "vbm_build_device_fill")
     return Grid(hdr, blob)
 
 

@@ -127,3 +127,19 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
         assert fn(h, FAKE_DEV, sc + 4 * N * 4, sc, 4, 0, None) == ALIAS   # head overlap
         # (N+1) * C * 4 bytes past the 32-bit sidecar offsets
         assert fn(h, FAKE_DEV, sc, out_far, 200000, 0, None) == SIZE
+
+
+def test_device_build_validation_before_any_hip_call():
+    lib = vbm.load_library()
+    hdr = vbm.GridHeader()
+    ws = ctypes.c_uint64()
+    assert lib.vbm_build_device_workspace(-1, ctypes.byref(ws)) == ARG
+    assert lib.vbm_build_device_workspace(10, None) == ARG
+    assert lib.vbm_build_device_workspace(1 << 33, ctypes.byref(ws)) == SIZE
+    assert lib.vbm_build_device_plan(None, 4, 7, FAKE_DEV, 1 << 20, ctypes.byref(hdr), None) == ARG
+    assert lib.vbm_build_device_plan(FAKE_DEV, 4, 7, None, 1 << 20, ctypes.byref(hdr), None) == ARG
+    assert lib.vbm_build_device_plan(FAKE_DEV, 4, 7, FAKE_DEV, 1 << 20, None, None) == ARG
+    assert lib.vbm_build_device_plan(FAKE_DEV, 4, 5, FAKE_DEV, 1 << 20, ctypes.byref(hdr), None) == ARG
+    assert lib.vbm_build_device_plan(FAKE_DEV, -3, 7, FAKE_DEV, 1 << 20, ctypes.byref(hdr), None) == ARG
+    assert lib.vbm_build_device_fill(None, 4, FAKE_DEV, 1 << 20, FAKE_DEV, None) == ARG
+    assert lib.vbm_build_device_fill(ctypes.byref(hdr), 4, FAKE_DEV, 1 << 20, FAKE_DEV, None) == ARG  # no magic
