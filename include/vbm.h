@@ -306,6 +306,27 @@ int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_width, void*
 int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_workspace, uint64_t workspace_bytes,
                           void* d_blob, void* stream);
 
+/*
+ * The device-side build without any allocation, for callers that cannot
+ * allocate device memory (tight loops, harnesses that forbid hipMalloc): plan
+ * and fill in one call, with the workspace in a static array of the library on
+ * the current GPU instead of a caller workspace.
+ *   d_ijk, n, log2_width, grid, stream: as vbm_build_device_plan (this call
+ *              waits for the stream once, as the plan does)
+ *   d_blob     caller-owned device memory of blob_capacity bytes; filled when
+ *              blob_capacity >= grid->blob_bytes
+ * Limit: n <= 1,048,576 coordinates (a 48 MiB array that every GPU the library
+ * runs on holds until the process ends).  Calls on one GPU share that array:
+ * calls that overlap in time on the same GPU (other host threads, other
+ * streams) race and must not be issued.
+ * Errors: as the plan and fill; VBM_ERR_SIZE also for n above the limit, and
+ * for d_blob NULL or blob_capacity below grid->blob_bytes (grid then holds the
+ * header, so the caller knows the size; nothing is written to d_blob).
+ * Calls no hipMalloc, hipFree or allocating library routine.
+ */
+int vbm_build_device_static(const int32_t* d_ijk, int64_t n, int log2_width, void* d_blob, uint64_t blob_capacity,
+                            vbm_grid* grid, void* stream);
+
 /* Static English text for a status code. */
 const char* vbm_strerror(int status);
 

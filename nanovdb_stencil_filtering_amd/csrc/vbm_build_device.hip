@@ -28,6 +28,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 #include <rocprim/device/device_select.hpp>
@@ -335,6 +338,34 @@ __global__ void __launch_bounds__(256) k_fill_blocks(uint64_t L, uint64_t N, int
   }
 }
 
+// Workspace of vbm_build_device_static, for callers that cannot allocate: a
+// static array on every GPU the library runs on (held until the process
+// ends), reached from host code only through the address hipGetSymbolAddress
+// returns for the current device.
+constexpr uint64_t kStaticMaxCoords = uint64_t(1) << 20;
+constexpr uint64_t kStaticScratchBytes = uint64_t(48) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Address of `scratch` on the current device, looked up once per device.
+int static_scratch(void** ptr) {
+  static std::mutex lock;
+  static std::vector<void*> per_device;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VBM_ERR_HIP;
+  std::lock_guard<std::mutex> guard(lock);
+  if (per_device.size() <= size_t(dev)) per_device.resize(size_t(dev) + 1, nullptr);
+  if (!per_device[size_t(dev)]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return VBM_ERR_HIP;
+    }
+    per_device[size_t(dev)] = p;
+  }
+  *ptr = per_device[size_t(dev)];
+  return VBM_OK;
+}
+
 uint32_t grid_for(uint64_t items) {
   const uint64_t g = (items + 255) / 256;
   return uint32_t(g < 1 ? 1 : (g > 8192 ? 8192 : g));
@@ -479,4 +510,23 @@ extern "C" int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_wo
                        reinterpret_cast<uint64_t*>(blob + grid->off_block_jump));
   }
   return vbm_host::launch_status();
+}
+
+extern "C" int vbm_build_device_static(const int32_t* d_ijk, int64_t n, int log2_width, void* d_blob,
+                                       uint64_t blob_capacity, vbm_grid* grid, void* stream) {
+  if (!grid || n < 0 || (n > 0 && !d_ijk)) return VBM_ERR_ARG;
+  if (log2_width < 6 || log2_width > 9) return VBM_ERR_ARG;
+  if (uint64_t(n) > kStaticMaxCoords) return VBM_ERR_SIZE;
+  void* ws = nullptr;
+  int rc = static_scratch(&ws);
+  if (rc) return rc;
+  uint64_t temp = 0;
+  if (temp_storage_bytes(uint64_t(n), static_cast<hipStream_t>(stream), &temp) != hipSuccess) {
+    (void)hipGetLastError();
+    return VBM_ERR_HIP;
+  }
+  if (workspace_layout(uint64_t(n), temp).total > kStaticScratchBytes) return VBM_ERR_SIZE;
+  if ((rc = vbm_build_device_plan(d_ijk, n, log2_width, ws, kStaticScratchBytes, grid, stream))) return rc;
+  if (!d_blob || blob_capacity < grid->blob_bytes) return VBM_ERR_SIZE;  // grid tells the size needed
+  return vbm_build_device_fill(grid, n, ws, kStaticScratchBytes, d_blob, stream);
 }

@@ -39,7 +39,8 @@ STATUS = {0: "VBM_OK", -1: "VBM_ERR_ARG", -2: "VBM_ERR_SIZE", -3: "VBM_ERR_ALIGN
 
 EXPORTED = ("vbm_build", "vbm_free_blob", "vbm_build_metadata", "vbm_decode", "vbm_decode_sweep", "vbm_stencil_indices",
             "vbm_box_filter", "vbm_cross_filter", "vbm_axis_filter", "vbm_weno_filter",
-            "vbm_build_device_workspace", "vbm_build_device_plan", "vbm_build_device_fill", "vbm_strerror")
+            "vbm_build_device_workspace", "vbm_build_device_plan", "vbm_build_device_fill",
+            "vbm_build_device_static", "vbm_strerror")
 
 
 class VbmError(RuntimeError):
@@ -102,6 +103,8 @@ def load_library():
     lib.vbm_build_device_plan.argtypes = [P, I64, I, P, ctypes.c_uint64, GP, P]
     lib.vbm_build_device_fill.restype = I
     lib.vbm_build_device_fill.argtypes = [GP, I64, P, ctypes.c_uint64, P, P]
+    lib.vbm_build_device_static.restype = I
+    lib.vbm_build_device_static.argtypes = [P, I64, I, P, ctypes.c_uint64, GP, P]
     lib.vbm_weno_filter.restype = I
     lib.vbm_weno_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_strerror.restype = ctypes.c_char_p
