@@ -106,6 +106,46 @@ def headline_kernel(channels):
     return "k_box_cached<%d, %s, true>" % (channels, "true" if channels % 4 == 0 else "false")
 
 
+def time_builds(coords, log2w, reps, dev):
+    """Wall-clock seconds (median of reps) of the host build (vbm_build, C++ on one
+    host core) and of the device-side build (plan + fill, coordinates already in
+    device memory, workspace and blob allocated beforehand), and the device blob's
+    equality with the host's."""
+    import ctypes
+    import numpy as np
+    import torch
+    from nanovdb_stencil_filtering_amd import vbm
+    lib = vbm.load_library()
+    host_t = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        hdr, host_blob = vbm.build_host(coords, log2w)
+        host_t.append(time.perf_counter() - t0)
+    c = torch.from_numpy(np.ascontiguousarray(coords, np.int32)).to(dev)
+    n = c.shape[0]
+    need = ctypes.c_uint64()
+    assert lib.vbm_build_device_workspace(n, ctypes.byref(need)) == 0
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    blob = torch.empty(int(hdr.blob_bytes), dtype=torch.uint8, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    dev_t = []
+    for _ in range(reps + 1):  # the first call warms up (code objects, allocator)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h2 = vbm.GridHeader()
+        assert lib.vbm_build_device_plan(ctypes.c_void_p(c.data_ptr()), n, log2w, ctypes.c_void_p(ws.data_ptr()),
+                                         need.value, ctypes.byref(h2), st) == 0
+        assert lib.vbm_build_device_fill(ctypes.byref(h2), n, ctypes.c_void_p(ws.data_ptr()), need.value,
+                                         ctypes.c_void_p(blob.data_ptr()), st) == 0
+        torch.cuda.synchronize()
+        dev_t.append(time.perf_counter() - t0)
+    same = bytes(h2) == bytes(hdr) and bool(np.array_equal(blob.cpu().numpy(), host_blob))
+    med = lambda v: sorted(v)[len(v) // 2]
+    return {"host_ms": round(1e3 * med(host_t), 3), "device_ms": round(1e3 * med(dev_t[1:]), 3),
+            "speedup": round(med(host_t) / med(dev_t[1:]), 1), "n_coords": int(n), "blob_identical": same,
+            "workspace_bytes": int(need.value)}
+
+
 def time_launches(fn, n_sets, steps, warmup):
     """Mean ms per launch of fn(k) for k = 0..steps-1 over rotating buffer sets."""
     import torch
@@ -340,6 +380,10 @@ def main():
             t, _ = time_graph(meta, 1, 20, 5)
             assert torch.equal(gw.blob, blob0) and int(total.item()) == N, "metadata replay changed the grid"
             rec("build_metadata_W%d" % gw.width, t, 2 * 80 * L + (4 + gw.width // 8) * gw.n_blocks)
+        # grid build from coordinates: host (vbm_build) vs device (vbm_build_device_plan + _fill)
+        extra["build_cfg_shell_W128"] = time_builds(coords, 7, 3, dev)
+        log("  build cfg-shell W128: host %.1f ms, device %.2f ms" % (extra["build_cfg_shell_W128"]["host_ms"],
+                                                                     extra["build_cfg_shell_W128"]["device_ms"]))
         # decode: select-based vs the sweep it replaced, every width (the pages' A/B), on the
         # cfg-shell and on the decode-stress topology (20,000 leaves, occupancy 2-100 %)
         stress = inputs.leaf_bernoulli_coords(4, **inputs.STRESS)
@@ -387,6 +431,8 @@ def main():
         del scs, outs
         log("bench: generating the narrow band")
         band = inputs.band_coords(5, **inputs.BAND)
+        band_build = time_builds(band, 9, 1, dev)
+        log("  build band W512: host %.1f ms, device %.2f ms" % (band_build["host_ms"], band_build["device_ms"]))
         gb = vbm.build(band, 9, device=dev)
         Nb = gb.n_active
         log("bench: band N=%d leaves=%d blocks=%d" % (Nb, gb.n_leaves, gb.n_blocks))
@@ -404,7 +450,7 @@ def main():
             "ms": round(tb, 4), "GBps": round(abb / (tb * 1e-3) / 1e9, 1),
             "hbm_frac": round(abb / (tb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "voxel_ch_per_s": float("%.4e" % (Nb * 16 / (tb * 1e-3))), "n_active": Nb, "n_leaves": gb.n_leaves,
-            "kernel": headline_kernel(16), "alg_bytes_per_launch": abb}
+            "kernel": headline_kernel(16), "alg_bytes_per_launch": abb, "build": band_build}
         extra["band_box_cached_streaming_W512_C16"] = band
         log("  band box cached streaming W512 C16: %.4f ms, %.1f GB/s" % (tb, abb / (tb * 1e-3) / 1e9))
         del scb, outb, gb

@@ -144,10 +144,13 @@ void vbm_free_blob(void* host_blob);
  * edit leaf masks in place on the device and rebuild with this call as long as
  * every leaf keeps at least one active voxel and the total stays n_active (the
  * block sections are sized by it); the new total is written to *d_total (a
- * device u64; NULL to skip) so the caller can check.  The tree sections (root,
- * upper, lower) and the leaf origins are read-only here.  The jumpMap words
- * hold the per-256-leaf partial sums of the leafFirst scan until the last
- * kernel rewrites them, so the call needs no workspace.  Asynchronous on
+ * device u64; NULL to skip) so the caller can check, and *d_total is set to
+ * UINT64_MAX instead if an edit left a leaf without any active voxel (the grid
+ * is then unusable: a leaf index would no longer follow from the jumpMap rank).
+ * The tree sections (root, upper, lower) and the leaf origins are read-only
+ * here.  The jumpMap words hold the per-256-leaf partial sums of the leafFirst
+ * scan until they are cleared for the block metadata, so the call needs no
+ * workspace.  Asynchronous on
  * `stream`; the blob must not be in use by other work on other streams.
  * Errors: VBM_ERR_ARG, VBM_ERR_HIP.
  */

@@ -923,8 +923,9 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
 //     words 0..k) and leafFirst (1 + active voxels in all earlier leaves);
 //   * per block the leaf owning its first index and the jumpMap bits of the
 //     slots >= 1 whose index starts a leaf.
-// Three launches: per-leaf counts and directories, one workgroup scanning the
-// counts in place into leafFirst, one wave per block for its metadata.
+// Five launches: per-leaf counts and directories (with per-256-leaf sums), one
+// workgroup scanning the sums, every leaf's leafFirst, the jumpMap words
+// cleared, and the block metadata scattered by the leaves.
 
 struct MutableGrid {
   Leaf* leaves;
@@ -937,12 +938,16 @@ struct MutableGrid {
 
 // Per leaf: prefix directory, and the active count parked in `first` for the
 // scan; per workgroup of 256 leaves the sum of their counts, parked in
-// block_jump[workgroup] (the jumpMap words are rewritten by k_meta_blocks; they
-// number at least N / 64 >= L / 64 > L / 256).
+// block_jump[workgroup] (the jumpMap words are rewritten at the end; they
+// number at least N / 64 >= L / 64 > L / 256).  A leaf left without any active
+// voxel by an edit marks its group sum with kEmptyLeaf (bit 63; a group sum is
+// at most 256 * 512).
+constexpr uint64_t kEmptyLeaf = uint64_t(1) << 63;
+
 __global__ void __launch_bounds__(256) k_meta_counts(MutableGrid m) {
-  __shared__ uint32_t group_sum;
+  __shared__ uint32_t group_sum, empty;
   const uint32_t l = blockIdx.x * blockDim.x + threadIdx.x;
-  if (threadIdx.x == 0) group_sum = 0;
+  if (threadIdx.x == 0) group_sum = empty = 0;
   __syncthreads();
   if (l < m.n_leaves) {
     Leaf& L = m.leaves[l];
@@ -959,22 +964,32 @@ __global__ void __launch_bounds__(256) k_meta_counts(MutableGrid m) {
     L.prefix = uint64_t(lo) | (uint64_t(hi) << 32);
     L.first = count;
     atomicAdd(&group_sum, count);
+    if (count == 0) atomicOr(&empty, 1u);
   }
   __syncthreads();
-  if (threadIdx.x == 0) m.block_jump[blockIdx.x] = group_sum;
+  if (threadIdx.x == 0) m.block_jump[blockIdx.x] = group_sum | (empty ? kEmptyLeaf : 0);
 }
 
 // One workgroup: the G group sums in block_jump[0 .. G) become exclusive
-// prefix sums; *total = their sum (N).  Each work-item owns a contiguous run.
+// prefix sums; *total = their sum (N), or ~0 if a leaf is empty.  Each
+// work-item owns a contiguous run.
 __global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint32_t G, uint64_t* __restrict__ total) {
   __shared__ uint64_t part[1024];
+  __shared__ uint32_t empty;
   const uint32_t T = blockDim.x, t = threadIdx.x;
+  if (t == 0) empty = 0;
   const uint32_t per = (G + T - 1) / T;
   const uint32_t a = min(G, t * per), e = min(G, a + per);
   uint64_t s = 0;
-  for (uint32_t k = a; k < e; ++k) s += m.block_jump[k];
+  bool any_empty = false;
+  for (uint32_t k = a; k < e; ++k) {
+    const uint64_t v = m.block_jump[k];
+    any_empty |= (v & kEmptyLeaf) != 0;
+    s += v & ~kEmptyLeaf;
+  }
   part[t] = s;
   __syncthreads();
+  if (any_empty) atomicOr(&empty, 1u);
   for (uint32_t d = 1; d < T; d <<= 1) {  // inclusive scan of the runs' sums
     const uint64_t v = t >= d ? part[t - d] : 0;
     __syncthreads();
@@ -983,11 +998,11 @@ __global__ void __launch_bounds__(1024) k_meta_scan(MutableGrid m, uint32_t G, u
   }
   uint64_t run = t ? part[t - 1] : 0;
   for (uint32_t k = a; k < e; ++k) {
-    const uint64_t c = m.block_jump[k];
+    const uint64_t c = m.block_jump[k] & ~kEmptyLeaf;
     m.block_jump[k] = run;
     run += c;
   }
-  if (t == T - 1 && total) *total = part[T - 1];
+  if (t == T - 1 && total) *total = empty ? ~uint64_t(0) : part[T - 1];
 }
 
 // Per workgroup of 256 leaves: leafFirst = 1 + the group's offset + the
@@ -1007,34 +1022,30 @@ __global__ void __launch_bounds__(256) k_meta_first(MutableGrid m) {
   if (l < m.n_leaves) m.leaves[l].first = 1 + m.block_jump[blockIdx.x] + (sums[t] - count);
 }
 
-// One wave per block: the leaf owning index g0 = 1 + bW (binary search over
-// leafFirst), then the leaves starting inside the block set their jumpMap bits.
-__global__ void __launch_bounds__(64) k_meta_blocks(MutableGrid m) {
-  __shared__ uint32_t words[16];  // the block's jumpMap as 32-bit halves
-  const uint32_t b = blockIdx.x, lane = threadIdx.x;
-  const uint32_t W = 1u << m.log2w;
-  const uint64_t g0 = 1 + (uint64_t(b) << m.log2w);
-  if (lane < 2 * (W / 64)) words[lane] = 0;
-  uint32_t lo = 0, hi = m.n_leaves;  // first leaf with leafFirst > g0
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (m.leaves[mid].first <= g0) lo = mid + 1; else hi = mid;
-  }
-  const uint32_t first = lo - 1;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (uint32_t l = first + 1 + lane; l < m.n_leaves; l += 64) {
-    const uint64_t s = m.leaves[l].first - g0;
-    if (s >= W) break;  // leafFirst grows with l: later leaves start past the block
-    __hip_atomic_fetch_or(&words[s >> 5], 1u << (s & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (lane == 0) m.block_first_leaf[b] = first;
-  if (lane < W / 64)
-    m.block_jump[uint64_t(b) * (W / 64) + lane] = uint64_t(words[2 * lane]) | (uint64_t(words[2 * lane + 1]) << 32);
+// The jumpMap words are cleared once the scan's partial sums are consumed.
+__global__ void __launch_bounds__(256) k_meta_clear_jump(MutableGrid m) {
+  const uint64_t words = uint64_t(m.n_blocks) << (m.log2w - 6);
+  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < words; i += uint64_t(gridDim.x) * blockDim.x)
+    m.block_jump[i] = 0;
+}
+
+// Block metadata by scatter, one work-item per leaf (first index f, next
+// leaf's first index or N + 1 as its end): the leaf sets the jumpMap bit of
+// slot (f - 1) % W of block (f - 1) / W unless it starts that block, and is
+// firstLeafID of every block whose first index 1 + bW lies in [f, end).
+// Blocks are those of the header's N (ids past them are skipped).
+__global__ void __launch_bounds__(256) k_meta_scatter(MutableGrid m, uint64_t n_active) {
+  const uint32_t l = blockIdx.x * blockDim.x + threadIdx.x;
+  if (l >= m.n_leaves) return;
+  const uint64_t W = uint64_t(1) << m.log2w;
+  const uint64_t f = m.leaves[l].first;
+  const uint64_t end = l + 1 < m.n_leaves ? uint64_t(m.leaves[l + 1].first) : n_active + 1;
+  const uint64_t s = (f - 1) & (W - 1), b = (f - 1) >> m.log2w;
+  if (s != 0 && b < m.n_blocks)
+    atomicOr(reinterpret_cast<unsigned long long*>(&m.block_jump[(b << (m.log2w - 6)) + (s >> 6)]),
+             (unsigned long long)1 << (s & 63));
+  for (uint64_t bb = (f - 1 + W - 1) >> m.log2w; bb < m.n_blocks && 1 + (bb << m.log2w) < end; ++bb)
+    m.block_first_leaf[bb] = l;
 }
 
 __global__ void k_zero_index_row(float* __restrict__ out, uint32_t C) {
@@ -1388,12 +1399,17 @@ extern "C" int vbm_build_metadata(const vbm_grid* grid, void* d_blob, uint64_t* 
   m.log2w = grid->log2_width;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint32_t groups = (m.n_leaves + 255) / 256;
-  // the group sums live in the jumpMap words until k_meta_blocks rewrites them
+  // the group sums live in the jumpMap words until they are cleared for the scatter
   // (a grid with every leaf non-empty always has room: N / 64 >= L / 64 words)
   if (uint64_t(groups) > uint64_t(m.n_blocks) << (m.log2w - 6)) return VBM_ERR_ARG;
   hipLaunchKernelGGL(k_meta_counts, dim3(groups), dim3(256), 0, st, m);
   hipLaunchKernelGGL(k_meta_scan, dim3(1), dim3(1024), 0, st, m, groups, d_total);
   hipLaunchKernelGGL(k_meta_first, dim3(groups), dim3(256), 0, st, m);
-  if (m.n_blocks) hipLaunchKernelGGL(k_meta_blocks, dim3(m.n_blocks), dim3(64), 0, st, m);
+  if (m.n_blocks) {
+    const uint64_t words = uint64_t(m.n_blocks) << (m.log2w - 6);
+    const uint64_t wg = (words + 255) / 256;
+    hipLaunchKernelGGL(k_meta_clear_jump, dim3(uint32_t(wg < 4096 ? wg : 4096)), dim3(256), 0, st, m);
+    hipLaunchKernelGGL(k_meta_scatter, dim3(groups), dim3(256), 0, st, m, grid->n_active);
+  }
   return launch_status();
 }

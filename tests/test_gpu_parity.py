@@ -409,6 +409,20 @@ def test_build_metadata_after_in_place_edit():
         assert np.array_equal(u32(out), ref.box(sc).view(np.uint32))
 
 
+def test_build_metadata_reports_an_emptied_leaf():
+    """An in-place edit that clears every voxel of a leaf breaks rank = leaf-id
+    arithmetic; the rebuild reports it with a total of UINT64_MAX instead of
+    producing a silently wrong grid."""
+    coords = GRIDS["stress_small"]()
+    hdr, host = vbm.build_host(coords, 7)
+    g = vbm.Grid(hdr, torch.from_numpy(host.copy()).cuda())
+    assert int(vbm.build_metadata(g).item()) == hdr.n_active
+    L = hdr.n_leaves
+    g.blob[hdr.off_leaves:hdr.off_leaves + L * 128].view(L, 128)[L // 2, 0:64] = 0
+    say("build_metadata with leaf %d emptied" % (L // 2))
+    assert int(vbm.build_metadata(g).item()) == -1  # UINT64_MAX read as int64
+
+
 def test_filters_on_two_streams_interleaved():
     """The library keeps no state between calls: box filters of two sidecars
     (16 and 3 channels, so the split and the narrow kernels) launched
