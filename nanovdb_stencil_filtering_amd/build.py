@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libvbm.so")
+# checking build for the tests: every brick cell poisoned before each brick pass
+POISON_LIB = os.path.join(LIBDIR, "libvbm_poison.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,19 +64,23 @@ def _finish(job):
 def build() -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     k_obj = os.path.join(LIBDIR, "vbm_kernels.o")
+    p_obj = os.path.join(LIBDIR, "vbm_kernels_poison.o")
     d_obj = os.path.join(LIBDIR, "vbm_build_device.o")
     b_obj = os.path.join(LIBDIR, "vbm_build.o")
-    # the two HIP sources compile in parallel
-    jobs = [_start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_kernels.hip"), "-o", k_obj],
-                   os.path.join(LIBDIR, "resource_usage.txt")),
+    # the HIP sources compile in parallel
+    kernels = os.path.join(CSRC, "vbm_kernels.hip")
+    jobs = [_start([HIPCC, *HIP_FLAGS, "-c", kernels, "-o", k_obj], os.path.join(LIBDIR, "resource_usage.txt")),
+            _start([HIPCC, *HIP_FLAGS, "-DVBM_POISON_LDS=1", "-c", kernels, "-o", p_obj],
+                   os.path.join(LIBDIR, "resource_usage_poison.txt")),
             _start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_build_device.hip"), "-o", d_obj],
                    os.path.join(LIBDIR, "resource_usage_build_device.txt"))]
     _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "vbm_build.cpp"), "-o", b_obj])
     for j in jobs:
         _finish(j)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, d_obj, b_obj, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, objs in ((LIB, [k_obj, d_obj, b_obj]), (POISON_LIB, [p_obj, d_obj, b_obj])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -210,6 +210,28 @@ __device__ __forceinline__ void consume_touch(const f32x4 (&v)[N]) {
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
 #endif
 
+// Checking build (VBM_POISON_LDS=1, a separate library used by the tests only):
+// before every brick pass all cells of the bricks are overwritten with a
+// poison value, so a voxel that reads a plane the pass did not build (the
+// build resolves only the x planes the block reaches), or a cell left from an
+// earlier pass or an earlier workgroup, gives a wrong tap or a wrong sum --
+// a deterministic mismatch against the oracle, never an access outside a
+// buffer (raw taps copy the value out; filter offsets go through the
+// bounds-checked sidecar loads).  The x ranges, tables, staged records and
+// slot corners are written in full before their barrier and are not poisoned.
+#ifndef VBM_POISON_LDS
+#define VBM_POISON_LDS 0
+#endif
+
+__device__ __forceinline__ void poison_bricks(uint32_t* brick, uint32_t count, uint32_t value) {
+#if VBM_POISON_LDS
+  for (uint32_t c = threadIdx.x; c < count * kBrickCells; c += blockDim.x) brick[c] = value;
+  __syncthreads();
+#else
+  (void)brick; (void)count; (void)value;
+#endif
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  With VBM_XCD_REMAP the workgroup id is mapped so that XCD k works on
 // the contiguous block range [k * per, (k + 1) * per): neighbouring blocks
@@ -316,6 +338,7 @@ __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t*
       const uint32_t count = min(cap, span - j0);
       if (j0) __syncthreads();
       stage_table_range(g, first + j0, count, table);
+      poison_bricks(brick, count, 0xFFFFFFFEu);  // never an index
       build_bricks(g, table, count, xr + j0, 1u, 0u, brick);
       if (j - j0 < count) {
         const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
@@ -437,6 +460,7 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
       const uint32_t count = min(cap, span - j0);
       if (j0) __syncthreads();
       stage_table_range(g, first + j0, count, table);
+      poison_bricks(brick, count, side.row_bytes);  // offset of row 1: a wrong, in-bounds row
       build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
       if (j - j0 < count) {
         const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
@@ -567,6 +591,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       fill_table_range_staged(g, first + j0, count, staged, threadIdx.x, blockDim.x);
       __syncthreads();
     }
+    poison_bricks(brick, count, side.row_bytes);
     build_bricks_staged(staged, count, xr + j0, side.row_bytes, kInactive, brick);
 #else
     if (j0) {  // later passes: the whole block restages
@@ -574,6 +599,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       fill_table_range(g, first + j0, count, table, threadIdx.x, blockDim.x);
       __syncthreads();
     }
+    poison_bricks(brick, count, side.row_bytes);
     build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
 #endif
     for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {

@@ -19,6 +19,7 @@ There is no CPU fallback: if the library is not built, loading raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -26,6 +27,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libvbm.so")
+# checking build used by the tests (brick cells poisoned before every brick pass)
+POISON_LIB_PATH = os.path.join(_HERE, "_lib", "libvbm_poison.so")
 
 CACHED = 0x1
 STREAMING = 0x2
@@ -61,22 +64,36 @@ class GridHeader(ctypes.Structure):
     ]
 
 
-_lib = None
+_libs = {}
+_active_path = None  # set by using_library()
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Route every call of this module to the library at `path` (the tests use it
+    for the poisoned checking build) for the duration of the block."""
+    global _active_path
+    old = _active_path
+    _active_path = path
+    try:
+        yield load_library()
+    finally:
+        _active_path = old
 
 
 def load_library():
     """Load libvbm.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libvbm.so is not built (%s); run __graft_entry__.build() or "
-                          "python -m nanovdb_stencil_filtering_amd.build" % LIB_PATH)
+    path = _active_path or LIB_PATH
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run __graft_entry__.build() or "
+                          "python -m nanovdb_stencil_filtering_amd.build" % path)
     # torch brings its own HIP runtime; loading it first makes libvbm.so bind to
     # that same runtime, so torch's device pointers and streams are valid in the
     # library's launches (a second runtime would reject torch's stream handles).
     import torch  # noqa: F401
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     GP = ctypes.POINTER(GridHeader)
     lib.vbm_build.restype = I
@@ -109,7 +126,7 @@ def load_library():
     lib.vbm_weno_filter.argtypes = [GP, P, P, P, I, I, P]
     lib.vbm_strerror.restype = ctypes.c_char_p
     lib.vbm_strerror.argtypes = [I]
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 

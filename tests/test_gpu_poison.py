@@ -1,0 +1,77 @@
+"""The brick kernels of the checking build (libvbm_poison.so: every brick cell
+overwritten with a poison value before each brick pass) against the oracle.
+
+The box kernels build, per pass, only the x planes of each spanned leaf that
+the block's voxels reach, and leave the others as they were (from an earlier
+pass or an earlier workgroup on the CU).  With the poison, reading any cell the
+current pass did not build gives a wrong raw tap (0xFFFFFFFE) or adds the
+wrong row (row 1) -- a deterministic mismatch.  Grids and widths are chosen so
+that blocks span one to more than MaxCachedLeaves leaves, i.e. one pass,
+several passes per block, and the tree-walk fallback."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from nanovdb_stencil_filtering_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from nanovdb_stencil_filtering_amd import vbm  # noqa: E402
+from test_gpu_parity import GRIDS  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def test_poisoned_build_is_a_separate_library():
+    assert os.path.exists(vbm.POISON_LIB_PATH)
+    with open(vbm.POISON_LIB_PATH, "rb") as a, open(vbm.LIB_PATH, "rb") as b:
+        assert a.read() != b.read()
+
+
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "dense_cube", "stress_small", "hand", "one_per_leaf"])
+def test_poisoned_bricks_match_the_oracle(name):
+    coords = GRIDS[name]()
+    ref = oracle.OracleGrid(coords)
+    taps = ref.taps(27)
+    with vbm.using_library(vbm.POISON_LIB_PATH):
+        for log2w in (6, 7, 8, 9):
+            g = vbm.build(coords, log2w)
+            N = g.n_active
+            for flags in (vbm.CACHED, vbm.CACHED | vbm.STREAMING):
+                say("poisoned taps %s W=%d flags=%d" % (name, 1 << log2w, flags))
+                t = vbm.stencil_indices(g, 27, flags).cpu().numpy().view(np.uint64)
+                assert np.array_equal(t[:N], taps), (log2w, flags)
+            for C in (1, 3, 4, 8, 16):
+                sc = I.sidecar(800 + C, N, C)
+                want = ref.box(sc).view(np.uint32)
+                sct = torch.from_numpy(sc).cuda()
+                for flags in (vbm.CACHED, vbm.CACHED | vbm.STREAMING):
+                    out = torch.full_like(sct, float("nan"))
+                    vbm.box_filter(g, sct, flags, out=out)
+                    assert np.array_equal(out.cpu().numpy().view(np.uint32), want), (log2w, C, flags)
+
+
+def test_poisoned_headline_kernel_on_the_cfg_shell():
+    coords = I.shell_coords(**I.CFG_SHELL)
+    ref = oracle.OracleGrid(coords)
+    sc = I.sidecar(2, ref.n_active, 16)
+    want = ref.box(sc).view(np.uint32)
+    sct = torch.from_numpy(sc).cuda()
+    with vbm.using_library(vbm.POISON_LIB_PATH):
+        for log2w in (7, 9):
+            g = vbm.build(coords, log2w)
+            for flags in (vbm.CACHED, vbm.CACHED | vbm.STREAMING):
+                say("poisoned cfg-shell W=%d C=16 flags=%d" % (1 << log2w, flags))
+                out = torch.full_like(sct, float("nan"))
+                vbm.box_filter(g, sct, flags, out=out)
+                assert np.array_equal(out.cpu().numpy().view(np.uint32), want), (log2w, flags)
