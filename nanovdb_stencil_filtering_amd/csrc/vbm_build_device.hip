@@ -19,10 +19,10 @@
 //   4. counts of voxels, leaves (key >> 9), lower nodes (key >> 21) and root
 //      tiles (key >> 36), read back by the host, which lays out the blob.
 // Fill (vbm_build_device_fill), asynchronous:
-//   leaf ids, lower-node ids and root ranks by scans over start flags; leaf
-//   masks by atomic OR of each voxel's bit; one work-item per leaf writes its
-//   record (prefix directory from the mask) and its entries in the lower, upper
-//   and root sections; the block metadata by scatter: each leaf sets the jumpMap
+//   leaf ids, lower-node ids and root ranks by scans over start flags; one
+//   work-item per leaf builds its mask from its run of sorted keys and writes
+//   its record (prefix directory from the mask) and its entries in the lower,
+//   upper and root sections; the block metadata by scatter: each leaf sets the jumpMap
 //   bit of its first index and writes firstLeafID of every block whose first
 //   index it holds (no search).
 #include <hip/hip_runtime.h>
@@ -130,8 +130,12 @@ __device__ __forceinline__ int32_t wave_max(int32_t v) {
   return v;
 }
 
-// Root-tile bounding box and the coordinate range check.
+// Root-tile bounding box and the coordinate range check: per work-item, then
+// per wave (shuffles), then per workgroup (LDS), then one set of atomics per
+// workgroup (the grid is capped, so there are few).
 __global__ void __launch_bounds__(256) k_build_bounds(const int32_t* __restrict__ ijk, uint64_t n, BuildHeader* h) {
+  __shared__ int32_t wlo[4][3], whi[4][3];
+  __shared__ uint32_t wbad[4];
   int32_t lo[3] = {INT32_MAX, INT32_MAX, INT32_MAX}, hi[3] = {INT32_MIN, INT32_MIN, INT32_MIN};
   bool bad = false;
   for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x) {
@@ -149,13 +153,28 @@ __global__ void __launch_bounds__(256) k_build_bounds(const int32_t* __restrict_
     hi[a] = wave_max(hi[a]);
   }
   const bool any_bad = __any(bad);
+  const uint32_t w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-#pragma unroll
     for (int a = 0; a < 3; ++a) {
-      atomicMin(&h->lo[a], lo[a]);
-      atomicMax(&h->hi[a], hi[a]);
+      wlo[w][a] = lo[a];
+      whi[w][a] = hi[a];
     }
-    if (any_bad) atomicOr(&h->status, 1u);
+    wbad[w] = any_bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t waves = blockDim.x >> 6;
+    for (uint32_t k = 1; k < waves; ++k)
+      for (int a = 0; a < 3; ++a) {
+        wlo[0][a] = min(wlo[0][a], wlo[k][a]);
+        whi[0][a] = max(whi[0][a], whi[k][a]);
+        wbad[0] |= wbad[k];
+      }
+    for (int a = 0; a < 3; ++a) {
+      atomicMin(&h->lo[a], wlo[0][a]);
+      atomicMax(&h->hi[a], whi[0][a]);
+    }
+    if (wbad[0]) atomicOr(&h->status, 1u);
   }
 }
 
@@ -193,8 +212,10 @@ __global__ void __launch_bounds__(256) k_build_keys(const int32_t* __restrict__ 
   }
 }
 
-// Counts of leaves, lower nodes and root tiles among the N sorted unique keys.
+// Counts of leaves, lower nodes and root tiles among the N sorted unique keys:
+// per wave (shuffles), per workgroup (LDS), one set of atomics per workgroup.
 __global__ void __launch_bounds__(256) k_build_counts(const uint64_t* __restrict__ keys, BuildHeader* h) {
+  __shared__ uint32_t part[4][3];
   const uint64_t N = h->n_unique;
   uint32_t leaves = 0, lowers = 0, roots = 0;
   for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < N; i += uint64_t(gridDim.x) * blockDim.x) {
@@ -208,10 +229,20 @@ __global__ void __launch_bounds__(256) k_build_counts(const uint64_t* __restrict
     lowers += __shfl_xor(lowers, d);
     roots += __shfl_xor(roots, d);
   }
+  const uint32_t w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    atomicAdd(&h->n_leaves, (unsigned long long)leaves);
-    atomicAdd(&h->n_lower, (unsigned long long)lowers);
-    atomicAdd(&h->n_root, (unsigned long long)roots);
+    part[w][0] = leaves;
+    part[w][1] = lowers;
+    part[w][2] = roots;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long sum[3] = {0, 0, 0};
+    for (uint32_t k = 0; k < (blockDim.x >> 6); ++k)
+      for (int a = 0; a < 3; ++a) sum[a] += part[k][a];
+    atomicAdd(&h->n_leaves, sum[0]);
+    atomicAdd(&h->n_lower, sum[1]);
+    atomicAdd(&h->n_root, sum[2]);
   }
 }
 
@@ -254,18 +285,6 @@ struct BlobLeaf {  // the 128-byte leaf record of include/vbm.h
 };
 static_assert(sizeof(BlobLeaf) == 128, "leaf record");
 
-// Each voxel sets its bit in its leaf's value mask.
-__global__ void __launch_bounds__(256) k_fill_masks(const uint64_t* __restrict__ keys, uint64_t N, uint64_t L,
-                                                    const uint32_t* __restrict__ leaf_of_voxel, BlobLeaf* leaves) {
-  for (uint64_t i = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; i < N; i += uint64_t(gridDim.x) * blockDim.x) {
-    const uint32_t o = uint32_t(keys[i] & 511);
-    const uint32_t l = leaf_of_voxel[i] - 1;
-    if (l >= L) continue;
-    atomicOr(reinterpret_cast<unsigned long long*>(&leaves[l].mask[o >> 6]),
-             (unsigned long long)1 << (o & 63));
-  }
-}
-
 struct BlobSections {
   BlobLeaf* leaves;
   int32_t* root;       // 4 ints per tile: key x, y, z, upper node
@@ -274,10 +293,12 @@ struct BlobSections {
   uint32_t n_root, n_lower;
 };
 
-// One work-item per leaf: prefix directory, first index, origin, parents; the
-// leaf's entry in its lower node, and (for the first leaf of a lower node /
-// root tile) the entries of the upper node and the root table.
-__global__ void __launch_bounds__(256) k_fill_leaves(uint64_t L, const uint64_t* __restrict__ leaf_key,
+// One work-item per leaf: the value mask from the leaf's run of sorted keys
+// (voxels first .. next leaf's first - 1), prefix directory, first index,
+// origin, parents; the leaf's entry in its lower node, and (for the first leaf
+// of a lower node / root tile) the entries of the upper node and the root table.
+__global__ void __launch_bounds__(256) k_fill_leaves(uint64_t L, uint64_t N, const uint64_t* __restrict__ keys,
+                                                     const uint64_t* __restrict__ leaf_key,
                                                      const uint32_t* __restrict__ leaf_first,
                                                      const uint32_t* __restrict__ lower_id,
                                                      const uint32_t* __restrict__ root_rank, const BuildHeader* h,
@@ -285,11 +306,19 @@ __global__ void __launch_bounds__(256) k_fill_leaves(uint64_t L, const uint64_t*
   const TileBox box = tile_box(h);
   for (uint64_t l = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; l < L; l += uint64_t(gridDim.x) * blockDim.x) {
     BlobLeaf& rec = blob.leaves[l];
+    const uint64_t end = l + 1 < L ? uint64_t(leaf_first[l + 1]) - 1 : N;  // one past the leaf's last voxel
+    uint64_t mask[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (uint64_t i = uint64_t(leaf_first[l]) - 1; i < end && i < N; ++i) {
+      const uint32_t o = uint32_t(keys[i] & 511);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) mask[w] |= (o >> 6) == uint32_t(w) ? uint64_t(1) << (o & 63) : 0;
+    }
     uint64_t count = 0, dir = 0;
 #pragma unroll
-    for (int w = 0; w < 7; ++w) {
-      count += __popcll(rec.mask[w]);
-      dir |= count << (9 * w);
+    for (int w = 0; w < 8; ++w) {
+      rec.mask[w] = mask[w];
+      count += __popcll(mask[w]);
+      if (w < 7) dir |= count << (9 * w);
     }
     const uint64_t lk = leaf_key[l];
     const uint64_t tile = lk >> 27;  // position of the root tile in the bounding box
@@ -373,6 +402,13 @@ uint32_t grid_for(uint64_t items) {
 
 // Runs a rocPRIM call f(temp, bytes) after checking, with a size query
 // f(nullptr, bytes), that its temporary storage fits the workspace's.
+// Grid of the reduction kernels: at most 1024 workgroups of 256, so the
+// per-workgroup atomics stay few.
+uint32_t reduce_grid(uint64_t items) {
+  const uint64_t g = (items + 255) / 256;
+  return uint32_t(g < 1 ? 1 : (g > 1024 ? 1024 : g));
+}
+
 template <class F>
 int run_with_temp(void* temp, uint64_t temp_bytes, F&& f) {
   size_t need = 0;
@@ -416,7 +452,7 @@ extern "C" int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_w
   uint64_t* keys_a = reinterpret_cast<uint64_t*>(ws + w.keys_a);
   uint64_t* keys_b = reinterpret_cast<uint64_t*>(ws + w.keys_b);
   hipLaunchKernelGGL(k_build_init, dim3(1), dim3(64), 0, st, h);
-  if (n > 0) hipLaunchKernelGGL(k_build_bounds, dim3(grid_for(uint64_t(n))), dim3(256), 0, st, d_ijk, uint64_t(n), h);
+  if (n > 0) hipLaunchKernelGGL(k_build_bounds, dim3(reduce_grid(uint64_t(n))), dim3(256), 0, st, d_ijk, uint64_t(n), h);
   BuildHeader host;
   if (hipMemcpyAsync(&host, h, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
@@ -441,7 +477,7 @@ extern "C" int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_w
            return rocprim::unique(t, b, keys_b, keys_a, &h->n_unique, nn, rocprim::equal_to<uint64_t>(), st);
          })))
       return rc;
-    hipLaunchKernelGGL(k_build_counts, dim3(grid_for(uint64_t(n))), dim3(256), 0, st, keys_a, h);
+    hipLaunchKernelGGL(k_build_counts, dim3(reduce_grid(uint64_t(n))), dim3(256), 0, st, keys_a, h);
     if (hipMemcpyAsync(&host, h, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
       return VBM_ERR_HIP;
@@ -499,12 +535,11 @@ extern "C" int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_wo
     if ((rc = scan(leaf_key, 12, lower_id, L))) return rc;
     if ((rc = scan(leaf_key, 27, root_rank, L))) return rc;
     BlobLeaf* leaves = reinterpret_cast<BlobLeaf*>(blob + grid->off_leaves);
-    hipLaunchKernelGGL(k_fill_masks, dim3(grid_for(N)), dim3(256), 0, st, keys, N, L, leaf_of_voxel, leaves);
     BlobSections sec{leaves, reinterpret_cast<int32_t*>(blob + grid->off_root),
                      reinterpret_cast<uint32_t*>(blob + grid->off_upper),
                      reinterpret_cast<uint32_t*>(blob + grid->off_lower), grid->n_root, grid->n_lower};
-    hipLaunchKernelGGL(k_fill_leaves, dim3(grid_for(L)), dim3(256), 0, st, L, leaf_key, leaf_first, lower_id,
-                       root_rank, h, sec);
+    hipLaunchKernelGGL(k_fill_leaves, dim3(grid_for(L)), dim3(256), 0, st, L, N, keys, leaf_key, leaf_first,
+                       lower_id, root_rank, h, sec);
     hipLaunchKernelGGL(k_fill_blocks, dim3(grid_for(L)), dim3(256), 0, st, L, N, grid->log2_width, leaf_first,
                        reinterpret_cast<uint32_t*>(blob + grid->off_block_first_leaf),
                        reinterpret_cast<uint64_t*>(blob + grid->off_block_jump));

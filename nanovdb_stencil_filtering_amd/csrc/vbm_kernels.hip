@@ -537,10 +537,9 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   auto run = [&](uint32_t task, auto&& off) {
     const uint32_t slot = task / LANES, q = task % LANES;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    gather_box_pipelined<4, true, kPipe>(acc, side, [&](int t) {
-      const uint32_t o = off(t);
-      return o == kInactive ? o : o + 16 * q;
-    });
+    // an inactive tap's offset kInactive + 16 q (at most 0xFFFFFF30) is still at
+    // or beyond the buffer's size (checked on the host), so it reads zeros too
+    gather_box_pipelined<4, true, kPipe>(acc, side, [&](int t) { return off(t) + 16 * q; });
     const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + slot;
 #if VBM_NT_STORE
     f32x4* dst = reinterpret_cast<f32x4*>(out + idx * C + ch0) + q;
