@@ -412,11 +412,21 @@ __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
   if constexpr (STREAM) {
-    // each tap resolved by its tree walk as the gather pipeline asks for it
+    // taps streamed to the gather in three groups of nine (one x offset of the
+    // stencil each): the nine tree walks of a group are independent chains of
+    // dependent loads that overlap one another, and the group's offsets are
+    // consumed in tap order; at most nine are held, never the whole stencil
     const VoxelCoord p = voxel_coord(g, s);
-    gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) {
-      return tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
-    });
+#pragma unroll
+    for (int grp = 0; grp < 3; ++grp) {
+      uint32_t off[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int t = 9 * grp + k;
+        off[k] = tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+      }
+      gather_box_pipelined<CH, VEC, kPipe, 9>(acc, side, [&](int k) { return off[k]; });
+    }
   } else {
     uint64_t st[kBoxTaps];
     compute_box(g, s, st);
