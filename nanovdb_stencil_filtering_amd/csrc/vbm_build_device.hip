@@ -32,10 +32,6 @@
 #include <vector>
 
 #include <rocprim/device/device_radix_sort.hpp>
-#include <rocprim/device/device_scan.hpp>
-#include <rocprim/device/device_select.hpp>
-#include <rocprim/iterator/counting_iterator.hpp>
-#include <rocprim/iterator/transform_iterator.hpp>
 
 #include "vbm.h"
 #include "vbm_host_checks.hpp"
@@ -79,33 +75,145 @@ WorkspaceLayout workspace_layout(uint64_t n, uint64_t temp_bytes) {
   return w;
 }
 
-// Start flags over sorted keys: element i starts a new group of key >> shift.
+// ---------------------------------------------------------------------------
+// scans of start flags (duplicate removal and the leaf / lower-node / root ids)
+// ---------------------------------------------------------------------------
+// Inclusive scan of flag(i), i < count, in three launches: per tile of
+// kScanTile elements the number of set flags; one workgroup turns the tile
+// totals into exclusive offsets (and writes the grand total); per tile again
+// a block scan in index order, each element handed to sink(i, inclusive, flag).
+// Tiles are read 256 consecutive elements at a time (coalesced).
+constexpr uint32_t kScanThreads = 256;
+constexpr uint32_t kScanItems = 16;
+constexpr uint64_t kScanTile = uint64_t(kScanThreads) * kScanItems;
+
+uint64_t scan_tiles(uint64_t count) { return (count + kScanTile - 1) / kScanTile; }
+
+// Inclusive prefix sum over the 256 work-items of the workgroup; *total gets
+// the workgroup's sum.  All work-items must call it.
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* total) {
+  __shared__ uint32_t wave_sum[kScanThreads / 64];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(v, d);
+    if (lane >= uint32_t(d)) v += t;
+  }
+  if (lane == 63) wave_sum[wave] = v;
+  __syncthreads();
+  uint32_t before = 0, sum = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < kScanThreads / 64; ++k) {
+    before += k < wave ? wave_sum[k] : 0u;
+    sum += wave_sum[k];
+  }
+  __syncthreads();  // wave_sum is reused by the next call
+  *total = sum;
+  return before + v;
+}
+
+template <class Flag>
+__global__ void __launch_bounds__(kScanThreads) k_scan_tile_counts(Flag flag, uint64_t count, uint32_t* tile_sum) {
+  const uint64_t base = blockIdx.x * kScanTile;
+  uint32_t c = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < kScanItems; ++j) {
+    const uint64_t i = base + j * kScanThreads + threadIdx.x;
+    c += i < count ? flag(i) : 0u;
+  }
+  uint32_t total;
+  block_inclusive_scan(c, &total);
+  if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+}
+
+// One workgroup: tile_sum[0 .. T) becomes exclusive offsets; *grand = the sum.
+__global__ void __launch_bounds__(1024) k_scan_tile_offsets(uint32_t* tile_sum, uint64_t T, uint64_t* grand) {
+  __shared__ uint64_t part[1024];
+  const uint64_t t = threadIdx.x, per = (T + blockDim.x - 1) / blockDim.x;
+  const uint64_t a = t * per < T ? t * per : T, e = a + per < T ? a + per : T;
+  uint64_t sum = 0;
+  for (uint64_t k = a; k < e; ++k) sum += tile_sum[k];
+  part[t] = sum;
+  __syncthreads();
+  for (uint32_t d = 1; d < blockDim.x; d <<= 1) {
+    const uint64_t v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  uint64_t run = t ? part[t - 1] : 0;
+  for (uint64_t k = a; k < e; ++k) {
+    const uint32_t c = tile_sum[k];
+    tile_sum[k] = uint32_t(run);
+    run += c;
+  }
+  if (t == blockDim.x - 1 && grand) *grand = part[t];
+}
+
+template <class Flag, class Sink>
+__global__ void __launch_bounds__(kScanThreads) k_scan_apply(Flag flag, uint64_t count, const uint32_t* tile_off,
+                                                             Sink sink) {
+  const uint64_t base = blockIdx.x * kScanTile;
+  uint32_t running = tile_off[blockIdx.x];
+  for (uint32_t j = 0; j < kScanItems; ++j) {  // block-uniform trip count: every barrier is reached by all
+    const uint64_t i = base + j * kScanThreads + threadIdx.x;
+    const uint32_t f = i < count ? flag(i) : 0u;
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan(f, &total);
+    if (i < count) sink(i, running + incl, f);
+    running += total;
+  }
+}
+
+// Start flags over sorted keys: element i starts a new group of key >> shift,
+// i.e. keys i - 1 and i differ in a bit at or above `shift` (tested with a
+// mask, so no shift by a run-time count is emitted).
 struct KeyGroupStart {
   const uint64_t* keys;
-  uint32_t shift;
+  uint64_t high;  // ~((1 << shift) - 1): all ones for shift 0 (any difference starts a group)
   __host__ __device__ uint32_t operator()(uint64_t i) const {
-    return i == 0 || (keys[i] >> shift) != (keys[i - 1] >> shift) ? 1u : 0u;
+    return i == 0 || ((keys[i] ^ keys[i - 1]) & high) != 0 ? 1u : 0u;
+  }
+};
+KeyGroupStart group_start(const uint64_t* keys, uint32_t shift) {
+  return KeyGroupStart{keys, shift >= 64 ? uint64_t(0) : ~((uint64_t(1) << shift) - 1)};
+}
+
+// Sinks: the inclusive count itself, or (duplicate removal) the key moved to
+// its place among the distinct keys.
+struct WriteCount {
+  uint32_t* out;
+  __device__ void operator()(uint64_t i, uint32_t incl, uint32_t) const { out[i] = incl; }
+};
+struct CompactKey {
+  const uint64_t* in;
+  uint64_t* out;
+  __device__ void operator()(uint64_t i, uint32_t incl, uint32_t f) const {
+    if (f) out[incl - 1] = in[i];
   }
 };
 
-using Counting = rocprim::counting_iterator<uint64_t>;
-using StartFlags = rocprim::transform_iterator<Counting, KeyGroupStart, uint32_t>;
+// Inclusive scan of flag over count elements with sink; the tile totals live
+// in `tile_sum` (scan_tiles(count) entries).
+template <class Flag, class Sink>
+void flag_scan(Flag flag, uint64_t count, uint32_t* tile_sum, uint64_t* grand, Sink sink, hipStream_t st) {
+  const uint64_t T = scan_tiles(count);
+  if (T == 0) return;
+  hipLaunchKernelGGL(k_scan_tile_counts<Flag>, dim3(uint32_t(T)), dim3(kScanThreads), 0, st, flag, count, tile_sum);
+  hipLaunchKernelGGL(k_scan_tile_offsets, dim3(1), dim3(1024), 0, st, tile_sum, T, grand);
+  hipLaunchKernelGGL((k_scan_apply<Flag, Sink>), dim3(uint32_t(T)), dim3(kScanThreads), 0, st, flag, count, tile_sum,
+                     sink);
+}
 
-// Largest temporary storage the plan and fill ask rocPRIM for, for n keys.
+// Temporary storage of the plan and fill for n keys: the radix sort's (from
+// rocPRIM's size query) or the scans' tile totals, whichever is larger.
 hipError_t temp_storage_bytes(uint64_t n, hipStream_t st, uint64_t* bytes) {
-  size_t sort = 0, uniq = 0, scan = 0;
+  size_t sort = 0;
   uint64_t* k = nullptr;
-  uint64_t* cnt = nullptr;
-  uint32_t* out = nullptr;
   hipError_t e = rocprim::radix_sort_keys(nullptr, sort, k, k, n, 0, 64, st);
   if (e != hipSuccess) return e;
-  e = rocprim::unique(nullptr, uniq, k, k, cnt, n, rocprim::equal_to<uint64_t>(), st);
-  if (e != hipSuccess) return e;
-  StartFlags flags(Counting(0), KeyGroupStart{k, 9});
-  e = rocprim::inclusive_scan(nullptr, scan, flags, out, n, rocprim::plus<uint32_t>(), st);
-  if (e != hipSuccess) return e;
-  size_t m = sort > uniq ? sort : uniq;
-  *bytes = m > scan ? m : scan;
+  const uint64_t tiles = 4 * scan_tiles(n);
+  *bytes = sort > tiles ? sort : tiles;
   return hipSuccess;
 }
 
@@ -307,17 +415,17 @@ __global__ void __launch_bounds__(256) k_fill_leaves(uint64_t L, uint64_t N, con
   for (uint64_t l = blockIdx.x * uint64_t(blockDim.x) + threadIdx.x; l < L; l += uint64_t(gridDim.x) * blockDim.x) {
     BlobLeaf& rec = blob.leaves[l];
     const uint64_t end = l + 1 < L ? uint64_t(leaf_first[l + 1]) - 1 : N;  // one past the leaf's last voxel
-    uint64_t mask[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t half[16] = {};  // the mask as 32-bit halves (32-bit shifts only)
     for (uint64_t i = uint64_t(leaf_first[l]) - 1; i < end && i < N; ++i) {
       const uint32_t o = uint32_t(keys[i] & 511);
 #pragma unroll
-      for (int w = 0; w < 8; ++w) mask[w] |= (o >> 6) == uint32_t(w) ? uint64_t(1) << (o & 63) : 0;
+      for (int k = 0; k < 16; ++k) half[k] |= (o >> 5) == uint32_t(k) ? 1u << (o & 31) : 0u;
     }
     uint64_t count = 0, dir = 0;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      rec.mask[w] = mask[w];
-      count += __popcll(mask[w]);
+      rec.mask[w] = uint64_t(half[2 * w]) | (uint64_t(half[2 * w + 1]) << 32);
+      count += __popc(half[2 * w]) + __popc(half[2 * w + 1]);
       if (w < 7) dir |= count << (9 * w);
     }
     const uint64_t lk = leaf_key[l];
@@ -360,9 +468,8 @@ __global__ void __launch_bounds__(256) k_fill_blocks(uint64_t L, uint64_t N, int
     const uint64_t f = leaf_first[l];
     const uint64_t end = l + 1 < L ? uint64_t(leaf_first[l + 1]) : N + 1;  // one past the leaf's last index
     const uint64_t s = (f - 1) & (W - 1), b = (f - 1) >> log2w;
-    if (s != 0)
-      atomicOr(reinterpret_cast<unsigned long long*>(&block_jump[b * words + s / 64]),
-               (unsigned long long)1 << (s % 64));
+    if (s != 0)  // the bit's 32-bit half of the jumpMap word (32-bit shifts only)
+      atomicOr(reinterpret_cast<uint32_t*>(&block_jump[b * words + s / 64]) + ((s >> 5) & 1), 1u << (s & 31));
     for (uint64_t bb = (f - 1 + W - 1) >> log2w; 1 + (bb << log2w) < end; ++bb) block_first_leaf[bb] = uint32_t(l);
   }
 }
@@ -473,10 +580,8 @@ extern "C" int vbm_build_device_plan(const int32_t* d_ijk, int64_t n, int log2_w
            return rocprim::radix_sort_keys(t, b, keys_a, keys_b, nn, 0, key_bits, st);
          })))
       return rc;
-    if ((rc = run_with_temp(temp, w.temp_bytes, [&](void* t, size_t& b) {
-           return rocprim::unique(t, b, keys_b, keys_a, &h->n_unique, nn, rocprim::equal_to<uint64_t>(), st);
-         })))
-      return rc;
+    // duplicates removed: every key that differs from its predecessor moves to its place
+    flag_scan(group_start(keys_b, 0), nn, static_cast<uint32_t*>(temp), &h->n_unique, CompactKey{keys_b, keys_a}, st);
     hipLaunchKernelGGL(k_build_counts, dim3(reduce_grid(uint64_t(n))), dim3(256), 0, st, keys_a, h);
     if (hipMemcpyAsync(&host, h, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
@@ -521,19 +626,13 @@ extern "C" int vbm_build_device_fill(const vbm_grid* grid, int64_t n, void* d_wo
                      grid->off_upper / 16, (grid->off_upper + uint64_t(grid->n_upper) * 32768 * 4) / 16,
                      grid->off_lower / 16, (grid->off_lower + uint64_t(grid->n_lower) * 4096 * 4) / 16);
   if (N > 0) {
-    void* temp = ws + w.temp;
     // inclusive scans of start flags: leaf of each voxel, lower node and root rank of each leaf
-    auto scan = [&](const uint64_t* k, uint32_t shift, uint32_t* out, uint64_t count) {
-      return run_with_temp(temp, w.temp_bytes, [&](void* t, size_t& b) {
-        return rocprim::inclusive_scan(t, b, StartFlags(Counting(0), KeyGroupStart{k, shift}), out, count,
-                                       rocprim::plus<uint32_t>(), st);
-      });
-    };
-    if ((rc = scan(keys, 9, leaf_of_voxel, N))) return rc;
+    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + w.temp);
+    flag_scan(group_start(keys, 9), N, tiles, nullptr, WriteCount{leaf_of_voxel}, st);
     hipLaunchKernelGGL(k_fill_leaf_starts, dim3(grid_for(N)), dim3(256), 0, st, keys, N, L, leaf_of_voxel, leaf_key,
                        leaf_first);
-    if ((rc = scan(leaf_key, 12, lower_id, L))) return rc;
-    if ((rc = scan(leaf_key, 27, root_rank, L))) return rc;
+    flag_scan(group_start(leaf_key, 12), L, tiles, nullptr, WriteCount{lower_id}, st);
+    flag_scan(group_start(leaf_key, 27), L, tiles, nullptr, WriteCount{root_rank}, st);
     BlobLeaf* leaves = reinterpret_cast<BlobLeaf*>(blob + grid->off_leaves);
     BlobSections sec{leaves, reinterpret_cast<int32_t*>(blob + grid->off_root),
                      reinterpret_cast<uint32_t*>(blob + grid->off_upper),

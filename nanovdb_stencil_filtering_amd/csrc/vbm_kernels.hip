@@ -1076,9 +1076,9 @@ __global__ void __launch_bounds__(256) k_meta_scatter(MutableGrid m, uint64_t n_
   const uint64_t f = m.leaves[l].first;
   const uint64_t end = l + 1 < m.n_leaves ? uint64_t(m.leaves[l + 1].first) : n_active + 1;
   const uint64_t s = (f - 1) & (W - 1), b = (f - 1) >> m.log2w;
-  if (s != 0 && b < m.n_blocks)
-    atomicOr(reinterpret_cast<unsigned long long*>(&m.block_jump[(b << (m.log2w - 6)) + (s >> 6)]),
-             (unsigned long long)1 << (s & 63));
+  if (s != 0 && b < m.n_blocks)  // the bit's 32-bit half of the jumpMap word (32-bit shifts only)
+    atomicOr(reinterpret_cast<uint32_t*>(&m.block_jump[(b << (m.log2w - 6)) + (s >> 6)]) + ((s >> 5) & 1),
+             1u << (s & 31));
   for (uint64_t bb = (f - 1 + W - 1) >> m.log2w; bb < m.n_blocks && 1 + (bb << m.log2w) < end; ++bb)
     m.block_first_leaf[bb] = l;
 }

@@ -20,12 +20,17 @@ VAR_SHIFT64 = re.compile(r"v_(?:lshl|lshr|ashr)rev_[bi]64\s+v\[\d+:\d+\],\s*v\d+
 
 @pytest.fixture(scope="module")
 def device_asm(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("asm") / "vbm_kernels.s")
+    """Assembly of both HIP sources (the pipeline kernels and the device-side build)."""
+    d = tmp_path_factory.mktemp("asm")
     flags = [f for f in B.HIP_FLAGS if not f.startswith("-Rpass")]
-    subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(B.CSRC, "vbm_kernels.hip"),
-                    "-o", out], check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-    with open(out) as f:
-        return f.read()
+    text = []
+    for src in ("vbm_kernels.hip", "vbm_build_device.hip"):
+        out = str(d / (src + ".s"))
+        subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", out],
+                       check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+        with open(out) as f:
+            text.append(f.read())
+    return "\n".join(text)
 
 
 def kernels(asm):
@@ -43,7 +48,8 @@ def test_no_variable_count_64bit_vector_shifts(device_asm):
 
 def test_kernels_present(device_asm):
     names = [n for n, _ in kernels(device_asm)]
-    for k in ("k_decode", "k_decode_sweep", "k_taps", "k_box", "k_stencil"):
+    for k in ("k_decode", "k_decode_sweep", "k_taps", "k_box", "k_stencil", "k_weno", "k_meta_scatter",
+              "k_build_keys", "k_fill_leaves", "k_fill_blocks"):
         assert any(k in n for n in names), k
 
 
