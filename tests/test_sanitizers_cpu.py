@@ -5,7 +5,7 @@ g++ -fsanitize=address,undefined and driven over coordinate sets from the
 shared generators: empty, one voxel, duplicates, a random grid straddling root
 tiles, a tiny shell, the decode-stress topology, one voxel per leaf, and
 coordinates next to the 2^30 limit (host builder only; the oracle stops at
-2^20).  Any report aborts the driver."""
+2^20).  Any report aborts the test program."""
 import os
 import shutil
 import subprocess
