@@ -799,27 +799,45 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
 //   Godunov      centre > 0: max(max(left, 0)^2, min(right, 0)^2), else
 //                max(min(left, 0)^2, max(right, 0)^2); axes summed (x + y) + z.
 
+// x / d correctly rounded for a divisor d with rd = 1/d rounded: the product
+// x * rd corrected by its remainder, which one fma computes exactly
+// (Markstein's division step).  For d = 6 and d = 12 this is the IEEE quotient
+// for zero and for every finite x of magnitude at least 2^-124 (checked over
+// all fp32 x by tests/const_division_check.c); below that the quotient is
+// subnormal and the step can miss, and an infinite x gives NaN.
+__device__ __forceinline__ float div_const(float x, float d, float rd) {
+  const float q = x * rd;
+  return __builtin_fmaf(__builtin_fmaf(-q, d, x), rd, q);
+}
+
+// FAST divides by 6 and 12 with div_const, which the caller may choose only
+// when weno_const_div_ok holds for the tap values; otherwise every division is
+// the IEEE one.  Both give the same bits on that range.
+template <bool FAST>
 __device__ __forceinline__ float weno5_derivative(float a, float b, float c, float d, float e) {
-  const float p1 = ((2.0f * a - 7.0f * b) + 11.0f * c) / 6.0f;
-  const float p2 = ((-b + 5.0f * c) + 2.0f * d) / 6.0f;
-  const float p3 = ((2.0f * c + 5.0f * d) - e) / 6.0f;
+  auto by6 = [](float x) { return FAST ? div_const(x, 6.0f, 1.0f / 6.0f) : x / 6.0f; };
+  auto by12 = [](float x) { return FAST ? div_const(x, 12.0f, 1.0f / 12.0f) : x / 12.0f; };
+  const float p1 = by6((2.0f * a - 7.0f * b) + 11.0f * c);
+  const float p2 = by6((-b + 5.0f * c) + 2.0f * d);
+  const float p3 = by6((2.0f * c + 5.0f * d) - e);
   const float qa = (a - 2.0f * b) + c, ra = (a - 4.0f * b) + 3.0f * c;
   const float qb = (b - 2.0f * c) + d, rb = b - d;
   const float qc = (c - 2.0f * d) + e, rc = (3.0f * c - 4.0f * d) + e;
-  const float ta = ((13.0f * (qa * qa)) / 12.0f + (ra * ra) * 0.25f) + 1.0e-6f;
-  const float tb = ((13.0f * (qb * qb)) / 12.0f + (rb * rb) * 0.25f) + 1.0e-6f;
-  const float tc = ((13.0f * (qc * qc)) / 12.0f + (rc * rc) * 0.25f) + 1.0e-6f;
+  const float ta = (by12(13.0f * (qa * qa)) + (ra * ra) * 0.25f) + 1.0e-6f;
+  const float tb = (by12(13.0f * (qb * qb)) + (rb * rb) * 0.25f) + 1.0e-6f;
+  const float tc = (by12(13.0f * (qc * qc)) + (rc * rc) * 0.25f) + 1.0e-6f;
   const float wa = 1.0f / (ta * ta), wb = 6.0f / (tb * tb), wc = 3.0f / (tc * tc);
   return ((wa * p1 + wb * p2) + wc * p3) / ((wa + wb) + wc);
 }
 
 // |grad u|^2 contribution of one axis from its seven values u[0..6] = u[-3..3].
+template <bool FAST>
 __device__ __forceinline__ float weno_axis_sq(const float (&u)[7], bool outside) {
   float d[6];
 #pragma unroll
   for (int j = 0; j < 6; ++j) d[j] = u[j + 1] - u[j];
-  const float left = weno5_derivative(d[0], d[1], d[2], d[3], d[4]);
-  const float right = weno5_derivative(d[5], d[4], d[3], d[2], d[1]);
+  const float left = weno5_derivative<FAST>(d[0], d[1], d[2], d[3], d[4]);
+  const float right = weno5_derivative<FAST>(d[5], d[4], d[3], d[2], d[1]);
   const float lo = outside ? (left > 0.0f ? left : 0.0f) : (left < 0.0f ? left : 0.0f);
   const float hi = outside ? (right < 0.0f ? right : 0.0f) : (right > 0.0f ? right : 0.0f);
   const float l2 = lo * lo, h2 = hi * hi;
@@ -834,6 +852,7 @@ __host__ __device__ constexpr int weno_tap(int a, int k) {
 }
 
 // The WENO consumer per channel from the 19 tap values v[0..18] of one channel.
+template <bool FAST>
 __device__ __forceinline__ float weno_norm_sq(const float (&v)[kAxisTaps]) {
   const bool outside = v[9] > 0.0f;
   float sum = 0.0f;
@@ -842,10 +861,35 @@ __device__ __forceinline__ float weno_norm_sq(const float (&v)[kAxisTaps]) {
     float u[7];
 #pragma unroll
     for (int k = 0; k < 7; ++k) u[k] = v[weno_tap(a, k)];
-    const float g2 = weno_axis_sq(u, outside);
+    const float g2 = weno_axis_sq<FAST>(u, outside);
     sum = a == 0 ? g2 : sum + g2;
   }
   return sum;
+}
+
+// Whether one channel's tap values allow the FAST divisions: each value zero
+// or of magnitude in [2^-40, 2^45] (the sum of magnitudes bounds them above
+// and is NaN or infinite when a value is; twice the magnitude bits less two,
+// wrapping for zero, bounds the nonzero ones below).  Every value is then a
+// multiple of 2^-63, and so is every difference, numerator and second
+// difference q formed from them by fp32 additions and small integer multiples;
+// a nonzero numerator or 13 q^2 is therefore at least 2^-63 resp. 13 * 2^-126
+// (above 2^-124), and all stay below 2^100: inside the range of div_const.
+__device__ __forceinline__ bool weno_const_div_ok(const float (&v)[kAxisTaps]) {
+  constexpr uint32_t kLow = 0x2B800000u;  // bits of 2^-40
+  float mag = 0.0f;
+  uint32_t low = 0xFFFFFFFFu;
+#pragma unroll
+  for (int t = 0; t < kAxisTaps; ++t) {
+    mag += __builtin_fabsf(v[t]);
+    low = min(low, (__builtin_bit_cast(uint32_t, v[t]) << 1) - 2u);
+  }
+  return mag <= 0x1p45f && low >= 2u * kLow - 2u;
+}
+
+// One channel: with the FAST divisions where the range check allows them.
+__device__ __forceinline__ float weno_channel(const float (&v)[kAxisTaps]) {
+  return weno_const_div_ok(v) ? weno_norm_sq<true>(v) : weno_norm_sq<false>(v);
 }
 
 // The WENO consumer kernel: one work-item per slot.  The 19 axis taps are
@@ -891,13 +935,28 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     f32x4 v4[S::kTaps];
     auto finish = [&](uint32_t q) {
       float r[4];
+      bool fast = true;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         __builtin_amdgcn_sched_barrier(0);
         float v[S::kTaps];
 #pragma unroll
         for (int t = 0; t < S::kTaps; ++t) v[t] = v4[t][c];
-        r[c] = weno_norm_sq(v);
+        fast = fast && weno_const_div_ok(v);
+        r[c] = weno_norm_sq<true>(v);
+      }
+      if (!fast) {  // a value outside that range: the four channels again with IEEE divisions
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {  // channel c sits in component 0 after c rotations
+          float v[S::kTaps];
+#pragma unroll
+          for (int t = 0; t < S::kTaps; ++t) {
+            v[t] = v4[t][0];
+            v4[t] = f32x4{v4[t][1], v4[t][2], v4[t][3], v4[t][0]};
+          }
+          const float exact = weno_norm_sq<false>(v);
+          r[0] = r[1], r[1] = r[2], r[2] = r[3], r[3] = exact;
+        }
       }
       reinterpret_cast<float4*>(out + idx * C)[q] = make_float4(r[0], r[1], r[2], r[3]);
     };
@@ -937,12 +996,12 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
       for (int t = 0; t < S::kTaps; ++t)
         v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t], 0, 0));
     }
-    out[idx * C] = weno_norm_sq(v);
+    out[idx * C] = weno_channel(v);
     for (uint32_t ch = 1; ch < C; ++ch) {
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t)
         v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t] + 4 * ch, 0, 0));
-      out[idx * C + ch] = weno_norm_sq(v);
+      out[idx * C + ch] = weno_channel(v);
     }
   }
 }

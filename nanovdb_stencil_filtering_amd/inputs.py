@@ -84,6 +84,40 @@ def sidecar_rows(seed: int, row0: int, row1: int, channels: int) -> np.ndarray:
     return v
 
 
+def wide_range_sidecar(seed: int, n_active: int, channels: int, fraction: float = 0.01) -> np.ndarray:
+    """A sidecar like ``sidecar`` in which a share ``fraction`` of the elements,
+    picked one by one, are drawn from the rest of the finite fp32 range instead
+    of [-1, 1), in six equally likely kinds: signed zeros, subnormals, normals
+    from 1e-37 to 1e-12, the magnitudes 2^-41, 2^-40, 2^-39, 2^44, 2^45, 2^46 and
+    the neighbours of 2^-40 and 2^45, large ones (4e13 .. 1e18), and huge ones
+    (1e19 .. 1e38, whose squares overflow).  Row 0 (the background) keeps the
+    ordinary value of each channel."""
+    rows = n_active + 1
+    n = rows * channels
+    bits = splitmix64(seed, np.arange(4 * n, dtype=np.uint64)).reshape(4, n)
+    ordinary = _uniform_pm1_f32(bits[0])
+    u = (bits[1] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53       # kind
+    w = (bits[2] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53       # magnitude
+    sign = np.where((bits[3] & np.uint64(1)) != 0, -1.0, 1.0)
+    pick = ((bits[3] >> np.uint64(1)) % np.uint64(8)).astype(np.int64)
+    edges = np.array([2.0 ** -40, float(np.nextafter(np.float32(2.0 ** -40), np.float32(0))), 2.0 ** 45,
+                      float(np.nextafter(np.float32(2.0 ** 45), np.float32(np.inf))), 2.0 ** -41, 2.0 ** 46,
+                      2.0 ** -39, 2.0 ** 44])
+    kinds = [0.0 * sign,
+             sign * w * 2.0 ** -126,                 # subnormal after rounding to fp32
+             sign * 10.0 ** (-37 + 25 * w),          # 1e-37 .. 1e-12
+             sign * edges[pick],
+             sign * 10.0 ** (13.6 + 4.4 * w),        # 4e13 .. 1e18
+             sign * 10.0 ** (19 + 19 * w)]           # 1e19 .. 1e38
+    v = ordinary.astype(np.float64)
+    for k, val in enumerate(kinds):
+        sel = (u >= fraction * k / len(kinds)) & (u < fraction * (k + 1) / len(kinds))
+        v = np.where(sel, val, v)
+    out = v.astype(np.float32).reshape(rows, channels)
+    out[0] = ordinary.reshape(rows, channels)[0]
+    return out
+
+
 def shell_coords(radius: float, half_thickness: float) -> np.ndarray:
     """All integer points p with | ||p|| - radius | <= half_thickness, centred on the origin.
 

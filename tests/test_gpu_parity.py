@@ -166,6 +166,30 @@ def test_weno_filter(name, C):
             assert np.array_equal(u32(out), want), (log2w, flags)
 
 
+@pytest.mark.parametrize("C", [1, 3, 4, 8])
+def test_weno_filter_wide_range_values(C):
+    """WENO consumer on values from the whole finite fp32 range (subnormals,
+    tiny, huge, the edges of the kernels' range check for their shortcut
+    divisions by 6 and 12), mixed element by element with ordinary ones, so
+    that waves hold lanes on both sides of that check: bit for bit against the
+    oracle, NaN as NaN."""
+    for name in ("tiny_shell", "dense_cube", "stress_small"):
+        for log2w in (7, 9):
+            g, ref = grid_pair(name, log2w)
+            for fraction in (0.01, 0.2):
+                sc = I.wide_range_sidecar(800 + C, g.n_active, C, fraction)
+                want = ref.weno(sc)
+                nan = np.isnan(want)
+                sct = torch.from_numpy(sc).cuda()
+                for flags in BOX_FLAGS:
+                    say("weno wide-range %s W=%d C=%d fraction=%g flags=%d" % (name, 1 << log2w, C, fraction, flags))
+                    out = torch.full_like(sct, 12345.0)
+                    vbm.weno_filter(g, sct, flags, out=out)
+                    got = out.cpu().numpy()
+                    assert np.array_equal(np.isnan(got), nan), (log2w, flags)
+                    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)), (log2w, flags)
+
+
 def test_constant_field_interior_is_27():
     g, ref = grid_pair("dense_cube", 7)
     sc = torch.full((g.n_active + 1, 1), 0.5, dtype=torch.float32, device="cuda")
