@@ -887,9 +887,19 @@ __device__ __forceinline__ bool weno_const_div_ok(const float (&v)[kAxisTaps]) {
   return mag <= 0x1p45f && low >= 2u * kLow - 2u;
 }
 
-// One channel: with the FAST divisions where the range check allows them.
+// One channel: with the FAST divisions where the range check allows them.  The
+// values enter the IEEE path through an empty register constraint, so that the
+// compiler cannot share its subexpressions with the FAST path and hoist them
+// above the branch (which held both paths' values live: 82 VGPRs against 60).
 __device__ __forceinline__ float weno_channel(const float (&v)[kAxisTaps]) {
-  return weno_const_div_ok(v) ? weno_norm_sq<true>(v) : weno_norm_sq<false>(v);
+  if (weno_const_div_ok(v)) return weno_norm_sq<true>(v);
+  float w[kAxisTaps];
+#pragma unroll
+  for (int t = 0; t < kAxisTaps; ++t) {
+    w[t] = v[t];
+    asm volatile("" : "+v"(w[t]));
+  }
+  return weno_norm_sq<false>(w);
 }
 
 // The WENO consumer kernel: one work-item per slot.  The 19 axis taps are
