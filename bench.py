@@ -102,8 +102,8 @@ def counted_traffic(path=PROFILE):
 def headline_kernel(channels):
     """Name of the kernel vbm_box_filter launches for the cached streaming box at these channels."""
     if channels in (8, 16):
-        return "k_box_cached_split<%d, true>" % channels
-    return "k_box_cached<%d, %s, true>" % (channels, "true" if channels % 4 == 0 else "false")
+        return "k_box_cached_split<%d, true, Sidecar>" % channels
+    return "k_box_cached<%d, %s, true, Sidecar>" % (channels, "true" if channels % 4 == 0 else "false")
 
 
 def time_builds(coords, log2w, reps, dev):
@@ -363,6 +363,16 @@ def main():
         # hot-cache figure (single buffer set; the Infinity Cache may serve it)
         t = time_launches(box_step(g, flags_cs, scs[:1], outs[:1]), 1, 20, 5)
         rec("box_cached_streaming_W%d_C%d_hot" % (W, C), t, ab, N * C)
+        # the same launch with the sidecar rows reached by 64-bit addresses (the path a
+        # sidecar of 4 GiB or more takes by itself): one row per work-item, no prefetch
+        t = time_launches(box_step(g, flags_cs | vbm.WIDE_ROWS, scs, outs), n_sets, 20, 5)
+        rec("box_cached_streaming_W%d_C%d_wide_rows" % (W, C), t, ab, N * C)
+        for ch in (1, 8):
+            scw, outw, nw = make_sets(ch)
+            abw = alg_bytes_filter(N, L, nb, W, ch)
+            t = time_launches(box_step(g, flags_cs | vbm.WIDE_ROWS, scw, outw), nw, 20, 5)
+            rec("box_cached_streaming_W%d_C%d_wide_rows" % (W, ch), t, abw, N * ch)
+            del scw, outw
         # device-side metadata build (leaf directories, leafFirst, block metadata)
         # (short kernels: timed by replaying a captured graph, see time_graph)
         lib = vbm.load_library()

@@ -64,6 +64,8 @@ typedef enum vbm_status {
 #define VBM_STREAMING 0x2     /* stream taps to the consumer (else materialise them first)     */
 #define VBM_OP_SUM 0x0        /* cross filter: sum of the 7 taps                                */
 #define VBM_OP_LAPLACIAN 0x4  /* cross filter: (sum of active faces) - 6*centre                 */
+#define VBM_WIDE_ROWS 0x8     /* filters: reach sidecar rows by 64-bit addresses even below 4 GiB
+                                 (taken by itself when (N+1)*C*4 >= 0xFFFFFF00 bytes)           */
 
 #define VBM_MAX_CACHED_LEAVES 16  /* openvdb PR #2263, "Notes": MaxCachedLeaves is 16           */
 #define VBM_GRID_MAGIC 0x314D4256u /* "VBM1" */
@@ -209,10 +211,17 @@ int vbm_stencil_indices(const vbm_grid* grid, const void* d_blob, int shape, int
  *   C          channels >= 1
  *   flags      VBM_CACHED | VBM_STREAMING in any combination (the four resolvers of
  *              openvdb PR #2263, "Summary" table)
+ *              and VBM_WIDE_ROWS (below)
  * All four variants give bit-identical outputs.
+ * Sidecar size: below 0xFFFFFF00 bytes ((N+1) * C * 4) the rows are read through
+ * a bounds-checked buffer resource with 32-bit offsets, an inactive tap being an
+ * offset past the end (reads zeros, no branch).  From that size on, or with
+ * VBM_WIDE_ROWS, they are read by 64-bit addresses (an inactive tap loads
+ * nothing) in chunks of 16, 8 or 4 channels (float4) or of one channel (buffers
+ * not 16-byte aligned): somewhat slower, same bits.  A row (C * 4 bytes) must
+ * fit in 32 bits.
  * Errors: VBM_ERR_ARG, VBM_ERR_ALIGN, VBM_ERR_ALIAS, VBM_ERR_HIP, and VBM_ERR_SIZE
- * when (N+1) * C * 4 bytes reach 0xFFFFFF00 (sidecar offsets are 32-bit; the
- * offsets above that mark inactive taps).
+ * when C * 4 exceeds 2^32 - 1.
  */
 int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
                    int flags, void* stream);
@@ -223,7 +232,7 @@ int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const float* d_side
  *   VBM_OP_SUM        out = fp32 sum, in cross order from +0, over the active taps
  *   VBM_OP_LAPLACIAN  out = (fp32 sum over the active face taps in cross order)
  *                           - fl(6 * centre)
- *   flags: VBM_CACHED, VBM_STREAMING and one op.  VBM_STREAMING streams the 7
+ *   flags: VBM_CACHED, VBM_STREAMING, VBM_WIDE_ROWS and one op.  VBM_STREAMING streams the 7
  *   taps into the gather (the forEachCrossStencil that openvdb PR #2263,
  *   "Notes", leaves out as a wash on its hardware); without it the taps are
  *   materialised (7 entries) first.  All forms give identical bits.
@@ -240,7 +249,8 @@ int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_si
  *   out[g*C + ch] = fp32 sum, in axis tap order (see vbm_stencil_indices) from
  *   +0, of sidecar[tap*C + ch] over the active taps of voxel g.
  *   flags: VBM_CACHED (table of the 7 leaf directions: a reach of 3 < 8 leaves
- *   the leaf in at most one axis) and VBM_STREAMING.  All forms give identical bits.
+ *   the leaf in at most one axis), VBM_STREAMING and VBM_WIDE_ROWS.  All forms
+ *   give identical bits.
  * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
  * VBM_ERR_ALIAS, VBM_ERR_HIP, VBM_ERR_SIZE (as vbm_box_filter).
  */
@@ -263,7 +273,8 @@ int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const float* d_sid
  *   the kernel); no contraction, correctly rounded division, denormals kept.
  *   flags: VBM_CACHED (the 7-direction table of the axis stencil) and
  *   VBM_STREAMING (taps resolved as their loads are issued instead of into an
- *   array first).  All forms give identical bits.  Row 0 of out is written as 0.
+ *   array first), and VBM_WIDE_ROWS (as vbm_box_filter; all channels in one
+ *   launch).  All forms give identical bits.  Row 0 of out is written as 0.
  * Buffers as vbm_box_filter.  Errors: VBM_ERR_ARG, VBM_ERR_ALIGN,
  * VBM_ERR_ALIAS, VBM_ERR_HIP, VBM_ERR_SIZE (as vbm_box_filter).
  */

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <type_traits>
 
 #include "vbm.h"
 #include "vbm_device.hpp"
@@ -29,43 +30,95 @@ using namespace vbm;
 namespace {
 
 // ---------------------------------------------------------------------------
-// sidecar access through a bounds-checked buffer resource
+// sidecar access
 // ---------------------------------------------------------------------------
-// Raw buffer loads whose offset is at or beyond num_records return zeros.  An
-// inactive tap carries the offset kInactive, so it adds +0 without a branch
-// or a pointer select.  Rows of the sidecar must therefore end below kInactive
-// bytes (checked on the host).
+// A kernel reaches sidecar rows through one of two access types, both handing
+// out a 32-bit handle per row:
+//   Sidecar      (sidecars below 4 GiB) a bounds-checked buffer resource; the
+//                handle is the row's byte offset.  Raw buffer loads whose offset
+//                is at or beyond num_records return zeros, so an inactive tap
+//                carries the offset kInactive and adds +0 without a branch or
+//                a pointer select.  Rows must end below kInactive bytes.
+//   WideSidecar  (any size) 64-bit addresses; the handle is the row's index,
+//                and an inactive tap's handle kNoRow loads nothing and reads
+//                zeros.  Buffer resources cannot replace it: their offsets are
+//                32-bit, and so is the address of an indexed (strided) load.
+// tap(idx): handle of a tap (index 0 = inactive, reads zeros); row(idx): handle
+// of row idx itself (row 0 included); load4 / load1: 16 / 4 bytes at byte
+// offset in_row of a row.
 constexpr uint32_t kInactive = 0xFFFFFF00u;
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer resource word 3
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef const f32x4 __attribute__((address_space(1))) global_f32x4;
+typedef const float __attribute__((address_space(1))) global_f32;
 
 struct Sidecar {
+  static constexpr bool kWide = false;
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t row_bytes;  // C * 4
+  static __device__ __forceinline__ Sidecar make(const float* sc, uint32_t bytes, uint32_t C, uint32_t ch0) {
+    Sidecar s;
+    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc + ch0), short(0), int(bytes - 4 * ch0),
+                                               int(kBufferFlags));
+    s.row_bytes = 4 * C;
+    return s;
+  }
+  __device__ __forceinline__ uint32_t tap(uint32_t idx) const { return idx ? idx * row_bytes : kInactive; }
+  __device__ __forceinline__ uint32_t row(uint32_t idx) const { return idx * row_bytes; }
+  __device__ __forceinline__ uint32_t inactive() const { return kInactive; }
+  __device__ __forceinline__ uint32_t brick_scale() const { return row_bytes; }  // brick cells hold handles
+  __device__ __forceinline__ f32x4 load4(uint32_t h, uint32_t in_row) const {
+    // whole-vector bit cast: indexing the u32 vector element by element made
+    // clang emit a single dword load for all four channels
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, h + in_row, 0, 0));
+  }
+  __device__ __forceinline__ float load1(uint32_t h, uint32_t in_row) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, h + in_row, 0, 0));
+  }
+};
+
+struct WideSidecar {
+  static constexpr bool kWide = true;
+  static constexpr uint32_t kNoRow = 0xFFFFFFFFu;  // never an index (N < 2^32 - 1)
+  const char* base;    // channel ch0 of row 0
+  uint32_t row_bytes;  // C * 4
+  static __device__ __forceinline__ WideSidecar make(const float* sc, uint32_t, uint32_t C, uint32_t ch0) {
+    return WideSidecar{reinterpret_cast<const char*>(sc + ch0), 4 * C};
+  }
+  __device__ __forceinline__ uint32_t tap(uint32_t idx) const { return idx ? idx : kNoRow; }
+  __device__ __forceinline__ uint32_t row(uint32_t idx) const { return idx; }
+  __device__ __forceinline__ uint32_t inactive() const { return kNoRow; }
+  __device__ __forceinline__ uint32_t brick_scale() const { return 1u; }
+  __device__ __forceinline__ const char* at(uint32_t h, uint32_t in_row) const {
+    return base + (uint64_t(h) * row_bytes + in_row);
+  }
+  __device__ __forceinline__ f32x4 load4(uint32_t h, uint32_t in_row) const {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (h != kNoRow) v = *(const global_f32x4*)(at(h, in_row));  // a global-memory load
+    return v;
+  }
+  __device__ __forceinline__ float load1(uint32_t h, uint32_t in_row) const {
+    float v = 0.0f;
+    if (h != kNoRow) v = *(const global_f32*)(at(h, in_row));
+    return v;
+  }
 };
 
 __device__ __forceinline__ Sidecar make_sidecar(const float* sc, uint32_t bytes, uint32_t C, uint32_t ch0) {
-  Sidecar s;
-  s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc + ch0), short(0), int(bytes - 4 * ch0),
-                                             int(kBufferFlags));
-  s.row_bytes = 4 * C;
-  return s;
+  return Sidecar::make(sc, bytes, C, ch0);
 }
 
-__device__ __forceinline__ uint32_t tap_offset(const Sidecar& s, uint32_t idx) {
-  return idx ? idx * s.row_bytes : kInactive;
-}
+__device__ __forceinline__ uint32_t tap_offset(const Sidecar& s, uint32_t idx) { return s.tap(idx); }
 
-// acc[c] += row[c] for the CH channels at byte offset `off` (kInactive: zeros).
-template <int CH, bool VEC>
-__device__ __forceinline__ void add_row(float (&acc)[CH], const Sidecar& s, uint32_t off) {
+// acc[c] += row[c] for the CH channels of handle h (an inactive tap: zeros),
+// from byte in_row of the row on.
+template <int CH, bool VEC, class SC>
+__device__ __forceinline__ void add_row(float (&acc)[CH], const SC& s, uint32_t h, uint32_t in_row = 0) {
   if constexpr (VEC && CH % 4 == 0) {
 #pragma unroll
     for (int q = 0; q < CH / 4; ++q) {
-      // whole-vector bit cast: indexing the u32 vector element by element made
-      // clang emit a single dword load for all four channels
-      const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off + 16 * q, 0, 0));
+      const f32x4 v = s.load4(h, in_row + 16 * q);
       acc[4 * q + 0] = acc[4 * q + 0] + v.x;
       acc[4 * q + 1] = acc[4 * q + 1] + v.y;
       acc[4 * q + 2] = acc[4 * q + 2] + v.z;
@@ -73,26 +126,24 @@ __device__ __forceinline__ void add_row(float (&acc)[CH], const Sidecar& s, uint
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      acc[c] = acc[c] + __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, off + 4 * c, 0, 0));
+    for (int c = 0; c < CH; ++c) acc[c] = acc[c] + s.load1(h, in_row + 4 * c);
   }
 }
 
-// The CH channels at byte offset `off`, loaded into registers (no use yet).
+// The CH channels of handle h, loaded into registers (no use yet).
 template <int CH, bool VEC>
 struct Row {
   static constexpr int kVec = (VEC && CH % 4 == 0) ? CH / 4 : 0;
   f32x4 v[kVec ? kVec : 1];
   float f[kVec ? 1 : CH];
-  __device__ __forceinline__ void load(const Sidecar& s, uint32_t off) {
+  template <class SC>
+  __device__ __forceinline__ void load(const SC& s, uint32_t h, uint32_t in_row = 0) {
     if constexpr (kVec) {
 #pragma unroll
-      for (int q = 0; q < kVec; ++q)
-        v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off + 16 * q, 0, 0));
+      for (int q = 0; q < kVec; ++q) v[q] = s.load4(h, in_row + 16 * q);
     } else {
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
-        f[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, off + 4 * c, 0, 0));
+      for (int c = 0; c < CH; ++c) f[c] = s.load1(h, in_row + 4 * c);
     }
   }
   __device__ __forceinline__ void add_to(float (&acc)[CH]) const {
@@ -114,13 +165,14 @@ struct Row {
 // Gather-accumulate of NT taps (default: the 27 box taps) in tap order, software pipelined:
 // the rows of taps t+1..t+D are in flight while tap t is added, and the
 // scheduler is fenced between steps so it cannot hoist all 27 rows at once
-// (which costs more registers than a wave can hold).  off(t) gives the byte
-// offset of tap t (kInactive for an inactive tap).
-template <int CH, bool VEC, int D, int NT = kBoxTaps, class Off>
-__device__ __forceinline__ void gather_box_pipelined(float (&acc)[CH], const Sidecar& s, Off&& off) {
+// (which costs more registers than a wave can hold).  off(t) gives the handle
+// of tap t (s.tap(index): an inactive tap reads zeros); the channels are read
+// from byte in_row of each row on.
+template <int CH, bool VEC, int D, int NT = kBoxTaps, class SC, class Off>
+__device__ __forceinline__ void gather_box_pipelined(float (&acc)[CH], const SC& s, Off&& off, uint32_t in_row = 0) {
   Row<CH, VEC> buf[D];
 #pragma unroll
-  for (int t = 0; t < D; ++t) buf[t].load(s, off(t));
+  for (int t = 0; t < D; ++t) buf[t].load(s, off(t), in_row);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     __builtin_amdgcn_sched_barrier(0);
@@ -129,7 +181,7 @@ __device__ __forceinline__ void gather_box_pipelined(float (&acc)[CH], const Sid
     // the tree walks of later taps and keeps all the rows live.  Emits nothing.
 #pragma unroll
     for (int c = 0; c < CH; ++c) asm volatile("" : "+v"(acc[c]));
-    if (t + D < NT) buf[t % D].load(s, off(t + D));
+    if (t + D < NT) buf[t % D].load(s, off(t + D), in_row);
   }
 }
 
@@ -158,18 +210,22 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
 // v[k], so that a later block finds its rows in the L2.  The caller consumes v
 // only at its very end (consume_touch), so no wave waits for these loads.
 // bn = 0xFFFFFFFF (or a block past the grid) loads nothing.
-template <int N>
-__device__ __forceinline__ void touch_block_rows(const DeviceGrid& g, const Sidecar& side, uint32_t bn,
-                                                 f32x4 (&v)[N]) {
-  const bool has = bn < g.n_blocks;
-  const uint64_t row0 = 1 + (uint64_t(has ? bn : 0u) << g.log2w);
-  const uint64_t rows = has ? min(uint64_t(1) << g.log2w, uint64_t(g.n_active) + 1 - row0) : 0;
-  const uint32_t pieces = uint32_t((rows * side.row_bytes + 15) / 16);
+template <int N, class SC>
+__device__ __forceinline__ void touch_block_rows(const DeviceGrid& g, const SC& side, uint32_t bn, f32x4 (&v)[N]) {
+  if constexpr (SC::kWide) {  // the wide path does not prefetch
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const uint32_t piece = threadIdx.x + k * blockDim.x;
-    const uint32_t off = piece < pieces ? uint32_t(row0) * side.row_bytes + 16 * piece : kInactive;
-    v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, off, 0, 0));
+    for (int k = 0; k < N; ++k) v[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
+    const bool has = bn < g.n_blocks;
+    const uint64_t row0 = 1 + (uint64_t(has ? bn : 0u) << g.log2w);
+    const uint64_t rows = has ? min(uint64_t(1) << g.log2w, uint64_t(g.n_active) + 1 - row0) : 0;
+    const uint32_t pieces = uint32_t((rows * side.row_bytes + 15) / 16);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint32_t piece = threadIdx.x + k * blockDim.x;
+      const uint32_t off = piece < pieces ? uint32_t(row0) * side.row_bytes + 16 * piece : kInactive;
+      v[k] = side.load4(off, 0);
+    }
   }
 }
 template <int N>
@@ -399,7 +455,7 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
 }
 
 // 27-tap box filter, tree-walk resolution, over channels [ch0, ch0 + CH).
-template <int CH, bool VEC, bool STREAM>
+template <int CH, bool VEC, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                    float* __restrict__ out, uint32_t C, uint32_t ch0) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
@@ -407,7 +463,7 @@ __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
   if (s.leaf == kSentinelLeaf) return;
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const SC side = SC::make(sc, sc_bytes, C, ch0);
   float acc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
@@ -423,21 +479,21 @@ __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const int t = 9 * grp + k;
-        off[k] = tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+        off[k] = side.tap(resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
       }
       gather_box_pipelined<CH, VEC, kPipe, 9>(acc, side, [&](int k) { return off[k]; });
     }
   } else {
     uint64_t st[kBoxTaps];
     compute_box(g, s, st);
-    gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return tap_offset(side, uint32_t(st[t])); });
+    gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return side.tap(uint32_t(st[t])); });
   }
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   store_row<CH, VEC>(out + idx * C + ch0, acc);
 }
 
 // 27-tap box filter through the brick cache (materialised or streamed taps).
-template <int CH, bool VEC, bool STREAM>
+template <int CH, bool VEC, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                     float* __restrict__ out, uint32_t C, uint32_t ch0, uint32_t cap) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
@@ -450,7 +506,7 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const SC side = SC::make(sc, sc_bytes, C, ch0);
   float acc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
@@ -460,7 +516,7 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
     if (valid) {  // per-tap tree walk
       const VoxelCoord p = voxel_coord(g, s);
       gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) {
-        return tap_offset(side, resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+        return side.tap(resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
       });
     }
   } else {
@@ -470,8 +526,8 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
       const uint32_t count = min(cap, span - j0);
       if (j0) __syncthreads();
       stage_table_range(g, first + j0, count, table);
-      poison_bricks(brick, count, side.row_bytes);  // offset of row 1: a wrong, in-bounds row
-      build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
+      poison_bricks(brick, count, side.row(1));  // handle of row 1: a wrong, in-bounds row
+      build_bricks(g, table, count, xr + j0, side.brick_scale(), side.inactive(), brick);
       if (j - j0 < count) {
         const uint32_t* corner = brick_corner(brick, j - j0, s.offset);
         if constexpr (STREAM) {
@@ -497,7 +553,7 @@ __global__ void __launch_bounds__(512) k_box_cached(DeviceGrid g, const float* _
 // has min(W * LANES, max(W, VBM_SPLIT_MAX)) work-items, each handling one or
 // more (slot, quarter) tasks.  STREAM: taps are streamed from the brick in tap
 // order; else the 27 taps are materialised into an array first.
-template <int CH, bool STREAM>
+template <int CH, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const float* __restrict__ sc,
                                                            uint32_t sc_bytes, float* __restrict__ out, uint32_t C,
                                                            uint32_t ch0, uint32_t cap) {
@@ -519,7 +575,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const SC side = SC::make(sc, sc_bytes, C, ch0);
   // Touch the own rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks
   // later (about two per CU), so that block finds them in the L2 instead of HBM;
   // near enough that they are still in the 4 MB L2 when it starts, far enough
@@ -535,9 +591,13 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
     for (int k = 0; k < 2; ++k) {
       const uint32_t piece = threadIdx.x + k * blockDim.x;  // 16-byte pieces of the block's W rows
       const uint64_t row = 1 + (uint64_t(bn) << g.log2w) + piece / LANES;
-      const uint32_t off = has && piece < W * LANES && row <= g.n_active
-                               ? uint32_t(row) * side.row_bytes + 16 * (piece % LANES) : kInactive;
-      ahead[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, off, 0, 0));
+      if constexpr (SC::kWide) {  // the wide path does not prefetch
+        ahead[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      } else {
+        const uint32_t off = has && piece < W * LANES && row <= g.n_active
+                                 ? uint32_t(row) * side.row_bytes + 16 * (piece % LANES) : kInactive;
+        ahead[k] = side.load4(off, 0);
+      }
     }
   }
   const uint32_t first = g.block_first_leaf[b];
@@ -547,9 +607,10 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   auto run = [&](uint32_t task, auto&& off) {
     const uint32_t slot = task / LANES, q = task % LANES;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    // an inactive tap's offset kInactive + 16 q (at most 0xFFFFFF30) is still at
-    // or beyond the buffer's size (checked on the host), so it reads zeros too
-    gather_box_pipelined<4, true, kPipe>(acc, side, [&](int t) { return off(t) + 16 * q; });
+    // bytes 16 q .. 16 q + 15 of each tap's row; an inactive tap's buffer offset
+    // kInactive + 16 q (at most 0xFFFFFF30) is still at or beyond the buffer's
+    // size (checked on the host), so it reads zeros too
+    gather_box_pipelined<4, true, kPipe>(acc, side, off, 16 * q);
     const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + slot;
 #if VBM_NT_STORE
     f32x4* dst = reinterpret_cast<f32x4*>(out + idx * C + ch0) + q;
@@ -588,7 +649,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       const uint32_t cell = info & 0xFFFF;
       const int x = L.origin[0] + int(cell / 100), y = L.origin[1] + int((cell / 10) % 10);
       const int z = L.origin[2] + int(cell % 10);
-      run(task, [&](int t) { return tap_offset(side, resolve_tree(g, x + box_di(t), y + box_dj(t), z + box_dk(t))); });
+      run(task, [&](int t) { return side.tap(resolve_tree(g, x + box_di(t), y + box_dj(t), z + box_dk(t))); });
     }
     return;
   }
@@ -600,16 +661,16 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       fill_table_range_staged(g, first + j0, count, staged, threadIdx.x, blockDim.x);
       __syncthreads();
     }
-    poison_bricks(brick, count, side.row_bytes);
-    build_bricks_staged(staged, count, xr + j0, side.row_bytes, kInactive, brick);
+    poison_bricks(brick, count, side.row(1));
+    build_bricks_staged(staged, count, xr + j0, side.brick_scale(), side.inactive(), brick);
 #else
     if (j0) {  // later passes: the whole block restages
       __syncthreads();  // the previous pass is done with the LDS
       fill_table_range(g, first + j0, count, table, threadIdx.x, blockDim.x);
       __syncthreads();
     }
-    poison_bricks(brick, count, side.row_bytes);
-    build_bricks(g, table, count, xr + j0, side.row_bytes, kInactive, brick);
+    poison_bricks(brick, count, side.row(1));
+    build_bricks(g, table, count, xr + j0, side.brick_scale(), side.inactive(), brick);
 #endif
     for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
       const uint32_t info = slot_corner[task / LANES];
@@ -633,7 +694,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
 // faces in cross order - fl(6 c)) and the 19-tap axis stencil (sum).  Taps by
 // tree walks or through the per-tap cached table; streamed into the gather
 // pipeline (STREAM) or materialised into an array first.
-template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM>
+template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                  float* __restrict__ out, uint32_t C, uint32_t ch0) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
@@ -652,7 +713,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
       cached = true;
     }
   }
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const SC side = SC::make(sc, sc_bytes, C, ch0);
   // Rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks later (blocks go
   // round-robin over the 8 XCDs here, hence the factor 8).  Measured on MI355X:
   // 3-6 % faster at 8 channels a work-item, 2-3 % slower at 1, so only the wide form.
@@ -674,14 +735,14 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
       const uint32_t j = s.leaf - first;
       const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
       gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
-        if (LAP && t == S::kCentre) return kInactive;
-        return tap_offset(side, resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+        if (LAP && t == S::kCentre) return side.inactive();
+        return side.tap(resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
       });
     } else {
       const VoxelCoord p = voxel_coord(g, s);
       gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
-        if (LAP && t == S::kCentre) return kInactive;
-        return tap_offset(side, resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+        if (LAP && t == S::kCentre) return side.inactive();
+        return side.tap(resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
       });
     }
   } else {
@@ -692,7 +753,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) {
       if (LAP && j == S::kCentre) continue;
-      add_row<CH, VEC>(acc, side, tap_offset(side, uint32_t(st[j])));
+      add_row<CH, VEC>(acc, side, side.tap(uint32_t(st[j])));
     }
   }
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
@@ -700,7 +761,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
     float centre[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) centre[c] = 0.0f;
-    add_row<CH, VEC>(centre, side, uint32_t(idx) * side.row_bytes);
+    add_row<CH, VEC>(centre, side, side.row(uint32_t(idx)));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const float six_c = 6.0f * centre[c];
@@ -717,7 +778,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
 // neighbour records staged (Cached), then every (slot, quarter) task resolves
 // its taps and gathers its 16 bytes per tap in tap order.  The workgroup has at
 // least W work-items.  Same taps, same order, same result as k_stencil.
-template <class S, int CH, bool CACHED, bool LAP, bool STREAM>
+template <class S, int CH, bool CACHED, bool LAP, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                        float* __restrict__ out, uint32_t C, uint32_t ch0) {
   static_assert(CH % 4 == 0 && CH >= 8, "split rows need whole float4 groups");
@@ -729,7 +790,7 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
   const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, ch0);
+  const SC side = SC::make(sc, sc_bytes, C, ch0);
   const uint32_t first = g.block_first_leaf[b];
   const uint32_t span = block_span(g, b);  // block-uniform: the barriers below are uniform
   const bool cached = CACHED && span <= kMaxCachedLeaves;
@@ -751,20 +812,20 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
       const Leaf& L = g.leaves[first + j];
       return resolve_tree(g, L.origin[0] + x + S::di(t), L.origin[1] + y + S::dj(t), L.origin[2] + z + S::dk(t));
     };
-    auto piece = [&](uint32_t idx) { return idx ? idx * side.row_bytes + 16 * q : kInactive; };
+    // bytes 16 q .. 16 q + 15 of each tap's row
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (STREAM) {
-      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return piece(tap(t)); });
+      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return side.tap(tap(t)); }, 16 * q);
     } else {
       uint32_t st[S::kTaps];
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t) st[t] = tap(t);
-      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return piece(st[t]); });
+      gather_box_pipelined<4, true, kPipe, S::kTaps>(acc, side, [&](int t) { return side.tap(st[t]); }, 16 * q);
     }
     const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + task / LANES;
     if constexpr (LAP) {
       float centre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      add_row<4, true>(centre, side, uint32_t(idx) * side.row_bytes + 16 * q);
+      add_row<4, true>(centre, side, side.row(uint32_t(idx)), 16 * q);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float six_c = 6.0f * centre[c];
@@ -907,7 +968,7 @@ __device__ __forceinline__ float weno_channel(const float (&v)[kAxisTaps]) {
 // either each as its value load is issued (STREAM) or all into an array first;
 // then the channels are processed four at a time (VEC: 16-byte loads and
 // stores) or one at a time, reusing the resolved taps.
-template <bool VEC, bool CACHED, bool STREAM>
+template <bool VEC, bool CACHED, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                               float* __restrict__ out, uint32_t C) {
   using S = AxisShape;
@@ -928,7 +989,7 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     }
   }
   if (!valid) return;
-  const Sidecar side = make_sidecar(sc, sc_bytes, C, 0);
+  const SC side = SC::make(sc, sc_bytes, C, 0);
   const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
   const uint32_t j = s.leaf - first;
   VoxelCoord p{0, 0, 0};
@@ -973,17 +1034,17 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     auto load = [&](uint32_t q) {
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t)
-        v4[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, row[t] + 16 * q, 0, 0));
+        v4[t] = side.load4(row[t], 16 * q);
     };
     if constexpr (STREAM) {  // first chunk: each tap resolved as its load is issued
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t) {
-        row[t] = resolve(t) * side.row_bytes;
-        v4[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(side.rsrc, row[t], 0, 0));
+        row[t] = side.row(resolve(t));
+        v4[t] = side.load4(row[t], 0);
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < S::kTaps; ++t) row[t] = resolve(t) * side.row_bytes;
+      for (int t = 0; t < S::kTaps; ++t) row[t] = side.row(resolve(t));
       load(0);
     }
     finish(0);
@@ -996,21 +1057,21 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     if constexpr (STREAM) {
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t) {
-        row[t] = resolve(t) * side.row_bytes;
-        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t], 0, 0));
+        row[t] = side.row(resolve(t));
+        v[t] = side.load1(row[t], 0);
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < S::kTaps; ++t) row[t] = resolve(t) * side.row_bytes;
+      for (int t = 0; t < S::kTaps; ++t) row[t] = side.row(resolve(t));
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t)
-        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t], 0, 0));
+        v[t] = side.load1(row[t], 0);
     }
     out[idx * C] = weno_channel(v);
     for (uint32_t ch = 1; ch < C; ++ch) {
 #pragma unroll
       for (int t = 0; t < S::kTaps; ++t)
-        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(side.rsrc, row[t] + 4 * ch, 0, 0));
+        v[t] = side.load1(row[t], 4 * ch);
       out[idx * C + ch] = weno_channel(v);
     }
   }
@@ -1201,12 +1262,19 @@ using vbm_host::launch_status;
 
 int check_float_buffers(const vbm_grid* grid, const float* sc, const float* out, int C) {
   if (!sc || !out || C < 1) return VBM_ERR_ARG;
-  if ((grid->n_active + 1) * uint64_t(C) * 4 > kInactive) return VBM_ERR_SIZE;
+  if (uint64_t(C) * 4 > 0xFFFFFFFFull) return VBM_ERR_SIZE;  // a row's byte size is 32-bit
   if ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 3) return VBM_ERR_ALIGN;
   const uint64_t bytes = (grid->n_active + 1) * uint64_t(C) * 4;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(sc), b0 = reinterpret_cast<uintptr_t>(out);
   if (a0 < b0 + bytes && b0 < a0 + bytes) return VBM_ERR_ALIAS;
   return VBM_OK;
+}
+
+// Whether a filter reaches its sidecar rows by 64-bit addresses: asked for, or
+// a sidecar whose (N+1) * C * 4 bytes do not end below the buffer-resource
+// offset kInactive that marks an inactive tap.
+bool wide_rows(const vbm_grid* grid, int C, int flags) {
+  return (flags & VBM_WIDE_ROWS) || (grid->n_active + 1) * uint64_t(C) * 4 > kInactive;
 }
 
 // Brick capacity (spanned leaves resolved per pass) for BlockWidth 2^log2w:
@@ -1235,12 +1303,29 @@ uint32_t split_capacity(int log2w) {
   return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_SPLIT_CAP_W128) : log2w == 8 ? 4u : uint32_t(VBM_SPLIT_CAP_W512);
 }
 
-template <bool CACHED, bool STREAM>
+template <bool CACHED, bool STREAM, bool WIDE = false>
 struct BoxLauncher {
+  static constexpr uint32_t kWideChunk = 16;  // widest channel chunk of the wide path
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
-    if constexpr (CACHED && VEC && (CH == 8 || CH == 16)) {
+    if constexpr (WIDE && CACHED && VEC && (CH == 8 || CH == 16)) {  // rows by 64-bit addresses
+      const uint32_t cap = split_capacity(g.log2w);
+      const uint32_t W = 1u << g.log2w;
+      const uint32_t tasks = W * (CH / 4);
+      const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
+      hipLaunchKernelGGL((k_box_cached_split<CH, STREAM, WideSidecar>), dim3(box_grid_size(g.n_blocks)),
+                         dim3(threads), split_lds_bytes(cap, W), st, g, sc, bytes, out, C, ch0, cap);
+    } else if constexpr (WIDE) {
+      if constexpr (CACHED) {
+        const uint32_t cap = brick_capacity(g.log2w);
+        hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM, WideSidecar>), dim3(box_grid_size(g.n_blocks)),
+                           dim3(1u << g.log2w), brick_lds_bytes(cap), st, g, sc, bytes, out, C, ch0, cap);
+      } else {
+        hipLaunchKernelGGL((k_box_plain<CH, VEC, STREAM, WideSidecar>), dim3(g.n_blocks), dim3(1u << g.log2w), 0,
+                           st, g, sc, bytes, out, C, ch0);
+      }
+    } else if constexpr (CACHED && VEC && (CH == 8 || CH == 16)) {
       const uint32_t cap = split_capacity(g.log2w);
       const uint32_t W = 1u << g.log2w;
       const uint32_t tasks = W * (CH / 4);
@@ -1258,16 +1343,21 @@ struct BoxLauncher {
   }
 };
 
-template <class S, bool CACHED, bool LAP, bool STREAM>
+template <class S, bool CACHED, bool LAP, bool STREAM, bool WIDE = false>
 struct StencilLauncher {
+  static constexpr uint32_t kWideChunk = VBM_STENCIL_SPLIT ? 16 : 8;  // one row per work-item at 16 would spill
   template <int CH, bool VEC>
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
+    using SC = std::conditional_t<WIDE, WideSidecar, Sidecar>;
     if constexpr (VBM_STENCIL_SPLIT && VEC && CH == 16) {  // at CH = 8 one work-item per row is faster
       const uint32_t W = 1u << g.log2w, tasks = W * (CH / 4);
       const uint32_t threads = tasks < 256 ? tasks : (W > 256 ? W : 256u);
-      hipLaunchKernelGGL((k_stencil_split<S, CH, CACHED, LAP, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(threads),
-                         0, st, g, sc, bytes, out, C, ch0);
+      hipLaunchKernelGGL((k_stencil_split<S, CH, CACHED, LAP, STREAM, SC>), dim3(box_grid_size(g.n_blocks)),
+                         dim3(threads), 0, st, g, sc, bytes, out, C, ch0);
+    } else if constexpr (WIDE) {
+      hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM, WideSidecar>), dim3(g.n_blocks),
+                         dim3(1u << g.log2w), 0, st, g, sc, bytes, out, C, ch0);
     } else {
       hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st,
                          g, sc, bytes, out, C, ch0);
@@ -1309,6 +1399,36 @@ void launch_channels(const DeviceGrid& g, const float* sc, float* out, int C, hi
       ch0 += 2;
     } else {
       L::template go<1, false>(g, sc, bytes, out, uc, ch0, st);
+      ch0 += 1;
+    }
+  }
+}
+
+// Channel chunks with rows reached by 64-bit addresses (a sidecar of 4 GiB or
+// more, or VBM_WIDE_ROWS): 16 (up to L::kWideChunk) / 8 / 4 channels as float4
+// when both buffers are 16-byte aligned and C is a multiple of 4, else one
+// channel at a time.
+template <class L>
+void launch_channels_wide(const DeviceGrid& g, const float* sc, float* out, int C, hipStream_t st) {
+  const bool vec = ((reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(out)) & 15) == 0 && C % 4 == 0;
+  const uint32_t uc = uint32_t(C);
+  for (uint32_t ch0 = 0; ch0 < uc;) {
+    const uint32_t left = uc - ch0;
+    if constexpr (L::kWideChunk >= 16) {
+      if (vec && left >= 16) {
+        L::template go<16, true>(g, sc, 0u, out, uc, ch0, st);
+        ch0 += 16;
+        continue;
+      }
+    }
+    if (vec && left >= 8) {
+      L::template go<8, true>(g, sc, 0u, out, uc, ch0, st);
+      ch0 += 8;
+    } else if (vec) {
+      L::template go<4, true>(g, sc, 0u, out, uc, ch0, st);
+      ch0 += 4;
+    } else {
+      L::template go<1, false>(g, sc, 0u, out, uc, ch0, st);
       ch0 += 1;
     }
   }
@@ -1386,7 +1506,7 @@ extern "C" int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const fl
   if (rc) return rc;
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
-  if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_WIDE_ROWS)) return VBM_ERR_ARG;
   if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
@@ -1395,22 +1515,36 @@ extern "C" int vbm_box_filter(const vbm_grid* grid, const void* d_blob, const fl
   }
   const DeviceGrid g = device_grid(grid, d_blob);
   const bool cached = flags & VBM_CACHED, streaming = flags & VBM_STREAMING;
-  if (cached && streaming) launch_channels<BoxLauncher<true, true>>(g, d_sidecar, d_out, C, st);
-  else if (cached) launch_channels<BoxLauncher<true, false>>(g, d_sidecar, d_out, C, st);
-  else if (streaming) launch_channels<BoxLauncher<false, true>>(g, d_sidecar, d_out, C, st);
-  else launch_channels<BoxLauncher<false, false>>(g, d_sidecar, d_out, C, st);
+  if (wide_rows(grid, C, flags)) {
+    if (cached && streaming) launch_channels_wide<BoxLauncher<true, true, true>>(g, d_sidecar, d_out, C, st);
+    else if (cached) launch_channels_wide<BoxLauncher<true, false, true>>(g, d_sidecar, d_out, C, st);
+    else if (streaming) launch_channels_wide<BoxLauncher<false, true, true>>(g, d_sidecar, d_out, C, st);
+    else launch_channels_wide<BoxLauncher<false, false, true>>(g, d_sidecar, d_out, C, st);
+  } else {
+    if (cached && streaming) launch_channels<BoxLauncher<true, true>>(g, d_sidecar, d_out, C, st);
+    else if (cached) launch_channels<BoxLauncher<true, false>>(g, d_sidecar, d_out, C, st);
+    else if (streaming) launch_channels<BoxLauncher<false, true>>(g, d_sidecar, d_out, C, st);
+    else launch_channels<BoxLauncher<false, false>>(g, d_sidecar, d_out, C, st);
+  }
   return launch_status();
 }
 
 // The 7-direction filters (cross, 19-tap axis): flags pick the resolver and
 // the delivery; LAP only for the cross.
 template <class S, bool LAP>
-void launch_stencil(const DeviceGrid& g, const float* sc, float* out, int C, bool cached, bool streaming,
+void launch_stencil(const DeviceGrid& g, const float* sc, float* out, int C, bool cached, bool streaming, bool wide,
                     hipStream_t st) {
-  if (cached && streaming) launch_channels<StencilLauncher<S, true, LAP, true>>(g, sc, out, C, st);
-  else if (cached) launch_channels<StencilLauncher<S, true, LAP, false>>(g, sc, out, C, st);
-  else if (streaming) launch_channels<StencilLauncher<S, false, LAP, true>>(g, sc, out, C, st);
-  else launch_channels<StencilLauncher<S, false, LAP, false>>(g, sc, out, C, st);
+  if (wide) {
+    if (cached && streaming) launch_channels_wide<StencilLauncher<S, true, LAP, true, true>>(g, sc, out, C, st);
+    else if (cached) launch_channels_wide<StencilLauncher<S, true, LAP, false, true>>(g, sc, out, C, st);
+    else if (streaming) launch_channels_wide<StencilLauncher<S, false, LAP, true, true>>(g, sc, out, C, st);
+    else launch_channels_wide<StencilLauncher<S, false, LAP, false, true>>(g, sc, out, C, st);
+  } else {
+    if (cached && streaming) launch_channels<StencilLauncher<S, true, LAP, true>>(g, sc, out, C, st);
+    else if (cached) launch_channels<StencilLauncher<S, true, LAP, false>>(g, sc, out, C, st);
+    else if (streaming) launch_channels<StencilLauncher<S, false, LAP, true>>(g, sc, out, C, st);
+    else launch_channels<StencilLauncher<S, false, LAP, false>>(g, sc, out, C, st);
+  }
 }
 
 extern "C" int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const float* d_sidecar, float* d_out, int C,
@@ -1419,7 +1553,7 @@ extern "C" int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const 
   if (rc) return rc;
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
-  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_OP_LAPLACIAN)) return VBM_ERR_ARG;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_OP_LAPLACIAN | VBM_WIDE_ROWS)) return VBM_ERR_ARG;
   if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
@@ -1428,8 +1562,9 @@ extern "C" int vbm_cross_filter(const vbm_grid* grid, const void* d_blob, const 
   }
   const DeviceGrid g = device_grid(grid, d_blob);
   const bool cached = flags & VBM_CACHED, streaming = flags & VBM_STREAMING;
-  if (flags & VBM_OP_LAPLACIAN) launch_stencil<CrossShape, true>(g, d_sidecar, d_out, C, cached, streaming, st);
-  else launch_stencil<CrossShape, false>(g, d_sidecar, d_out, C, cached, streaming, st);
+  const bool wide = wide_rows(grid, C, flags);
+  if (flags & VBM_OP_LAPLACIAN) launch_stencil<CrossShape, true>(g, d_sidecar, d_out, C, cached, streaming, wide, st);
+  else launch_stencil<CrossShape, false>(g, d_sidecar, d_out, C, cached, streaming, wide, st);
   return launch_status();
 }
 
@@ -1439,7 +1574,7 @@ extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const f
   if (rc) return rc;
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
-  if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_WIDE_ROWS)) return VBM_ERR_ARG;
   if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
@@ -1447,7 +1582,8 @@ extern "C" int vbm_axis_filter(const vbm_grid* grid, const void* d_blob, const f
     return launch_status();
   }
   const DeviceGrid g = device_grid(grid, d_blob);
-  launch_stencil<AxisShape, false>(g, d_sidecar, d_out, C, flags & VBM_CACHED, flags & VBM_STREAMING, st);
+  launch_stencil<AxisShape, false>(g, d_sidecar, d_out, C, flags & VBM_CACHED, flags & VBM_STREAMING,
+                                   wide_rows(grid, C, flags), st);
   return launch_status();
 }
 
@@ -1457,7 +1593,7 @@ extern "C" int vbm_weno_filter(const vbm_grid* grid, const void* d_blob, const f
   if (rc) return rc;
   rc = check_float_buffers(grid, d_sidecar, d_out, C);
   if (rc) return rc;
-  if (flags & ~(VBM_CACHED | VBM_STREAMING)) return VBM_ERR_ARG;
+  if (flags & ~(VBM_CACHED | VBM_STREAMING | VBM_WIDE_ROWS)) return VBM_ERR_ARG;
   if ((rc = check_kernel_memory({d_blob, d_sidecar, d_out}))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (grid->n_blocks == 0) {
@@ -1465,13 +1601,18 @@ extern "C" int vbm_weno_filter(const vbm_grid* grid, const void* d_blob, const f
     return launch_status();
   }
   const DeviceGrid g = device_grid(grid, d_blob);
-  const uint32_t bytes = uint32_t((uint64_t(g.n_active) + 1) * uint64_t(C) * 4);
+  const bool wide = wide_rows(grid, C, flags);
+  const uint32_t bytes = wide ? 0u : uint32_t((uint64_t(g.n_active) + 1) * uint64_t(C) * 4);
   const bool vec = ((reinterpret_cast<uintptr_t>(d_sidecar) | reinterpret_cast<uintptr_t>(d_out)) & 15) == 0 &&
                    C % 4 == 0;
   const bool cached = flags & VBM_CACHED, streaming = flags & VBM_STREAMING;
   const dim3 gd(g.n_blocks), bd(1u << g.log2w);
   const uint32_t uc = uint32_t(C);
-#define VBM_WENO_LAUNCH(V, CA, ST) hipLaunchKernelGGL((k_weno<V, CA, ST>), gd, bd, 0, st, g, d_sidecar, bytes, d_out, uc)
+#define VBM_WENO_LAUNCH(V, CA, ST)                                                                      \
+  do {                                                                                                  \
+    if (wide) hipLaunchKernelGGL((k_weno<V, CA, ST, WideSidecar>), gd, bd, 0, st, g, d_sidecar, bytes, d_out, uc); \
+    else hipLaunchKernelGGL((k_weno<V, CA, ST>), gd, bd, 0, st, g, d_sidecar, bytes, d_out, uc);      \
+  } while (0)
   if (vec) {
     if (cached && streaming) VBM_WENO_LAUNCH(true, true, true);
     else if (cached) VBM_WENO_LAUNCH(true, true, false);

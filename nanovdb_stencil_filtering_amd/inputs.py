@@ -84,6 +84,16 @@ def sidecar_rows(seed: int, row0: int, row1: int, channels: int) -> np.ndarray:
     return v
 
 
+def sidecar_at(seed: int, rows: np.ndarray, channels: int) -> np.ndarray:
+    """The given rows (any order) of ``sidecar(seed, n, channels)``, same values,
+    so that a few rows of a sidecar too large to hold can be produced alone."""
+    rows = np.asarray(rows, dtype=np.uint64).ravel()
+    k = (rows[:, None] * np.uint64(channels) + np.arange(channels, dtype=np.uint64)[None, :]).ravel()
+    v = _uniform_pm1_f32(splitmix64(seed, k)).reshape(rows.size, channels)
+    v[rows == 0] = 0.0
+    return v
+
+
 def wide_range_sidecar(seed: int, n_active: int, channels: int, fraction: float = 0.01) -> np.ndarray:
     """A sidecar like ``sidecar`` in which a share ``fraction`` of the elements,
     picked one by one, are drawn from the rest of the finite fp32 range instead

@@ -34,6 +34,7 @@ CACHED = 0x1
 STREAMING = 0x2
 OP_SUM = 0x0
 OP_LAPLACIAN = 0x4
+WIDE_ROWS = 0x8  # filters: sidecar rows by 64-bit addresses (taken by itself from 0xFFFFFF00 bytes on)
 MAX_CACHED_LEAVES = 16
 GRID_MAGIC = 0x314D4256
 

@@ -108,9 +108,11 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 19, 0, None, None) == ARG
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 27, 0x40, FAKE_DEV, None) == ARG
     assert lib.vbm_stencil_indices(h, FAKE_DEV, 7, vbm.OP_LAPLACIAN, FAKE_DEV, None) == ARG
-    assert lib.vbm_box_filter(h, FAKE_DEV, sc, out_far, 1, 0x8, None) == ARG
+    assert lib.vbm_box_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
     assert lib.vbm_box_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
     assert lib.vbm_cross_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
+    assert lib.vbm_axis_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
+    assert lib.vbm_weno_filter(h, FAKE_DEV, sc, out_far, 1, 0x10, None) == ARG
     assert lib.vbm_axis_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
     assert lib.vbm_axis_filter(ctypes.byref(bad), FAKE_DEV, sc, out_far, 1, 0, None) == ARG
     assert lib.vbm_weno_filter(h, FAKE_DEV, sc, out_far, 1, vbm.OP_LAPLACIAN, None) == ARG
@@ -125,8 +127,8 @@ def test_gpu_entry_points_reject_bad_arguments(grid_hdr):
         assert fn(h, FAKE_DEV, sc, sc, 4, 0, None) == ALIAS
         assert fn(h, FAKE_DEV, sc, sc + 4 * N * 4, 4, 0, None) == ALIAS   # tail overlap
         assert fn(h, FAKE_DEV, sc + 4 * N * 4, sc, 4, 0, None) == ALIAS   # head overlap
-        # (N+1) * C * 4 bytes past the 32-bit sidecar offsets
-        assert fn(h, FAKE_DEV, sc, out_far, 200000, 0, None) == SIZE
+        # a row of C * 4 bytes past 32 bits (larger sidecars are read by 64-bit addresses)
+        assert fn(h, FAKE_DEV, sc, out_far, 1 << 30, 0, None) == SIZE
 
 
 def test_device_build_validation_before_any_hip_call():

@@ -62,6 +62,6 @@ def test_counters_only_for_the_sources_they_were_taken_on(tmp_path):
 
 def test_headline_kernel_names():
     b = load_bench()
-    assert b.headline_kernel(16) == "k_box_cached_split<16, true>"
-    assert b.headline_kernel(8) == "k_box_cached_split<8, true>"
-    assert b.headline_kernel(1) == "k_box_cached<1, false, true>"
+    assert b.headline_kernel(16) == "k_box_cached_split<16, true, Sidecar>"
+    assert b.headline_kernel(8) == "k_box_cached_split<8, true, Sidecar>"
+    assert b.headline_kernel(1) == "k_box_cached<1, false, true, Sidecar>"

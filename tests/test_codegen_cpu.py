@@ -58,6 +58,10 @@ def test_vector_sidecar_loads_are_16_bytes(device_asm):
     extraction of the buffer-load vector once collapsed into one dword load
     reused for all four channels)."""
     for name, body in kernels(device_asm):
-        if "k_box" in name and "ILi16ELb1E" in name:
+        if "k_box" in name and "ILi16ELb1E" in name and "WideSidecar" in name:
+            # rows by 64-bit addresses: 16-byte global loads, no buffer resource at all
+            assert "global_load_dwordx4" in body, name
+            assert "buffer_load" not in body, name
+        elif "k_box" in name and "ILi16ELb1E" in name:
             assert "buffer_load_dwordx4" in body, name
             assert "buffer_load_dword " not in body.replace("buffer_load_dwordx4", ""), name

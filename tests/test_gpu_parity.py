@@ -244,6 +244,41 @@ def test_filters_on_unaligned_and_wide_buffers(C):
                 assert np.array_equal(u32(out), want[name].view(np.uint32)), (name, shift, flags)
 
 
+@pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small"])
+def test_wide_rows_match_the_oracle(name, C):
+    """Every filter with its sidecar rows reached by 64-bit addresses (the path a
+    sidecar of 4 GiB or more takes by itself; here forced with WIDE_ROWS) in
+    every resolver and delivery: bit for bit as the oracle, on 16-byte aligned
+    buffers (float4 chunks of 16 / 8 / 4 channels) and on buffers that are only
+    4-byte aligned (one channel at a time)."""
+    for log2w in (7, 9):
+        g, ref = grid_pair(name, log2w)
+        sc = I.sidecar(900 + C, g.n_active, C)
+        # a nonzero row 0: the WENO consumer's background, never read by the summing filters
+        sc[0] = np.linspace(-0.5, 0.25, C, dtype=np.float32)
+        want = {"box": ref.box(sc), "sum": ref.cross(sc, "sum"), "lap": ref.cross(sc, "laplacian"),
+                "axis": ref.axis(sc), "weno": ref.weno(sc)}
+        n = sc.size
+        for shift in (0, 1):  # float elements: 0 = 16-byte aligned, 1 = 4-byte aligned only
+            big_in = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
+            big_in[shift:] = torch.from_numpy(sc.ravel()).cuda()
+            sct = big_in[shift:].view(g.n_active + 1, C)
+            big_out = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
+            out = big_out[shift:].view(g.n_active + 1, C)
+            for flags in BOX_FLAGS:
+                wf = flags | vbm.WIDE_ROWS
+                say("wide rows %s W=%d C=%d shift=%d flags=%d" % (name, 1 << log2w, C, shift, wf))
+                for what, run in (("box", lambda: vbm.box_filter(g, sct, wf, out=out)),
+                                  ("sum", lambda: vbm.cross_filter(g, sct, wf, out=out)),
+                                  ("lap", lambda: vbm.cross_filter(g, sct, wf | vbm.OP_LAPLACIAN, out=out)),
+                                  ("axis", lambda: vbm.axis_filter(g, sct, wf, out=out)),
+                                  ("weno", lambda: vbm.weno_filter(g, sct, wf, out=out))):
+                    out.fill_(float("nan"))
+                    run()
+                    assert np.array_equal(u32(out), want[what].view(np.uint32)), (what, log2w, shift, flags)
+
+
 def test_extreme_coordinates_by_translation():
     """Coordinates near the library's limit (|c| < 2^30): the tiny shell moved by
     whole root tiles (4096 voxels) to within two tiles of +-2^30 on every axis.
