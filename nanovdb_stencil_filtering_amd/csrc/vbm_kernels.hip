@@ -998,7 +998,7 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t));
     return resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t));
   };
-  uint32_t row[S::kTaps];  // byte offset of each tap's row (index 0: row 0, the background)
+  uint32_t row[S::kTaps];  // handle of each tap's row (index 0: row 0, the background)
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
   if constexpr (VEC) {
     // one chunk of four channels: q-th float4 of every tap row, then the four
