@@ -4,7 +4,10 @@ hipcc compiles the kernels and the C-ABI launchers (vbm_kernels.hip) and the
 device-side grid build (vbm_build_device.hip) in parallel; g++ compiles the
 host grid builder (vbm_build.cpp); hipcc links them into
 nanovdb_stencil_filtering_amd/_lib/libvbm.so.  Kernel resource usage (VGPRs,
-SGPRs, scratch, LDS, occupancy) is written to _lib/resource_usage.txt.
+SGPRs, scratch, LDS, occupancy) is written to _lib/resource_usage.txt.  Two
+libraries for the tests are built beside it: libvbm_poison.so (the same
+library with every brick cell poisoned before each brick pass) and
+libvbm_divcheck.so (the GPU check of the WENO kernels' shortcut divisions).
 """
 from __future__ import annotations
 
@@ -20,6 +23,9 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libvbm.so")
 # checking build for the tests: every brick cell poisoned before each brick pass
 POISON_LIB = os.path.join(LIBDIR, "libvbm_poison.so")
+# GPU check of the WENO kernels' shortcut divisions (tests/division_check.hip)
+DIVCHECK_LIB = os.path.join(LIBDIR, "libvbm_divcheck.so")
+DIVCHECK_SRC = os.path.join(ROOT, "tests", "division_check.hip")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -73,10 +79,13 @@ def build() -> str:
             _start([HIPCC, *HIP_FLAGS, "-DVBM_POISON_LDS=1", "-c", kernels, "-o", p_obj],
                    os.path.join(LIBDIR, "resource_usage_poison.txt")),
             _start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_build_device.hip"), "-o", d_obj],
-                   os.path.join(LIBDIR, "resource_usage_build_device.txt"))]
+                   os.path.join(LIBDIR, "resource_usage_build_device.txt")),
+            _start([HIPCC, *HIP_FLAGS, "-shared", DIVCHECK_SRC, "-o", DIVCHECK_LIB + ".tmp%d" % os.getpid()],
+                   os.path.join(LIBDIR, "divcheck_build.txt"))]
     _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "vbm_build.cpp"), "-o", b_obj])
     for j in jobs:
         _finish(j)
+    os.replace(DIVCHECK_LIB + ".tmp%d" % os.getpid(), DIVCHECK_LIB)
     for lib, objs in ((LIB, [k_obj, d_obj, b_obj]), (POISON_LIB, [p_obj, d_obj, b_obj])):
         tmp = lib + ".tmp%d" % os.getpid()
         _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])

@@ -23,6 +23,7 @@
 
 #include "vbm.h"
 #include "vbm_device.hpp"
+#include "vbm_division.hpp"
 #include "vbm_host_checks.hpp"
 
 using namespace vbm;
@@ -860,24 +861,14 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
 //   Godunov      centre > 0: max(max(left, 0)^2, min(right, 0)^2), else
 //                max(min(left, 0)^2, max(right, 0)^2); axes summed (x + y) + z.
 
-// x / d correctly rounded for a divisor d with rd = 1/d rounded: the product
-// x * rd corrected by its remainder, which one fma computes exactly
-// (Markstein's division step).  For d = 6 and d = 12 this is the IEEE quotient
-// for zero and for every finite x of magnitude at least 2^-124 (checked over
-// all fp32 x by tests/const_division_check.c); below that the quotient is
-// subnormal and the step can miss, and an infinite x gives NaN.
-__device__ __forceinline__ float div_const(float x, float d, float rd) {
-  const float q = x * rd;
-  return __builtin_fmaf(__builtin_fmaf(-q, d, x), rd, q);
-}
-
-// FAST divides by 6 and 12 with div_const, which the caller may choose only
-// when weno_const_div_ok holds for the tap values; otherwise every division is
-// the IEEE one.  Both give the same bits on that range.
+// FAST divides by 6 and 12 and forms the three weights n / t^2 with the
+// shortcuts of vbm_division.hpp, which the caller may choose only when
+// weno_fast_ok holds for the tap values; otherwise every division is the IEEE
+// one.  Both give the same bits on that range.
 template <bool FAST>
 __device__ __forceinline__ float weno5_derivative(float a, float b, float c, float d, float e) {
-  auto by6 = [](float x) { return FAST ? div_const(x, 6.0f, 1.0f / 6.0f) : x / 6.0f; };
-  auto by12 = [](float x) { return FAST ? div_const(x, 12.0f, 1.0f / 12.0f) : x / 12.0f; };
+  auto by6 = [](float x) { return FAST ? vbm_div::div_const(x, 6.0f, 1.0f / 6.0f) : x / 6.0f; };
+  auto by12 = [](float x) { return FAST ? vbm_div::div_const(x, 12.0f, 1.0f / 12.0f) : x / 12.0f; };
   const float p1 = by6((2.0f * a - 7.0f * b) + 11.0f * c);
   const float p2 = by6((-b + 5.0f * c) + 2.0f * d);
   const float p3 = by6((2.0f * c + 5.0f * d) - e);
@@ -887,7 +878,15 @@ __device__ __forceinline__ float weno5_derivative(float a, float b, float c, flo
   const float ta = (by12(13.0f * (qa * qa)) + (ra * ra) * 0.25f) + 1.0e-6f;
   const float tb = (by12(13.0f * (qb * qb)) + (rb * rb) * 0.25f) + 1.0e-6f;
   const float tc = (by12(13.0f * (qc * qc)) + (rc * rc) * 0.25f) + 1.0e-6f;
-  const float wa = 1.0f / (ta * ta), wb = 6.0f / (tb * tb), wc = 3.0f / (tc * tc);
+  const float ya = ta * ta, yb = tb * tb, yc = tc * tc;
+  float wa, wb, wc;
+  if constexpr (FAST) {
+    wa = vbm_div::recip(ya);
+    wb = vbm_div::div_by_recip(6.0f, yb, vbm_div::recip(yb));
+    wc = vbm_div::div_by_recip(3.0f, yc, vbm_div::recip(yc));
+  } else {
+    wa = 1.0f / ya, wb = 6.0f / yb, wc = 3.0f / yc;
+  }
   return ((wa * p1 + wb * p2) + wc * p3) / ((wa + wb) + wc);
 }
 
@@ -929,14 +928,21 @@ __device__ __forceinline__ float weno_norm_sq(const float (&v)[kAxisTaps]) {
 }
 
 // Whether one channel's tap values allow the FAST divisions: each value zero
-// or of magnitude in [2^-40, 2^45] (the sum of magnitudes bounds them above
+// or of magnitude in [2^-40, 2^27] (the sum of magnitudes bounds them above
 // and is NaN or infinite when a value is; twice the magnitude bits less two,
 // wrapping for zero, bounds the nonzero ones below).  Every value is then a
 // multiple of 2^-63, and so is every difference, numerator and second
-// difference q formed from them by fp32 additions and small integer multiples;
-// a nonzero numerator or 13 q^2 is therefore at least 2^-63 resp. 13 * 2^-126
-// (above 2^-124), and all stay below 2^100: inside the range of div_const.
-__device__ __forceinline__ bool weno_const_div_ok(const float (&v)[kAxisTaps]) {
+// difference q formed from them by fp32 additions and small integer multiples:
+// a nonzero numerator or 13 q^2 is at least 2^-63 resp. 13 * 2^-126 (above
+// 2^-124) and all stay below 2^70, inside the range of div_const.  A
+// difference is at most 2^28, so q and r are at most 2^30 and 2^31, an
+// indicator (13 q^2) / 12 + r^2 / 4 below 2^61.1, and t^2 lies in
+// [1e-12, 2^123): inside [2^-40, 2^126), the range of recip and div_by_recip.
+// The one way the shortcuts part from IEEE division there, a candidate of -0
+// coming out +0, does not reach the output: a zero candidate adds nothing to
+// the nonzero sums it enters, and a zero derivative of either sign becomes +0
+// in Godunov's rule before it is squared.
+__device__ __forceinline__ bool weno_fast_ok(const float (&v)[kAxisTaps]) {
   constexpr uint32_t kLow = 0x2B800000u;  // bits of 2^-40
   float mag = 0.0f;
   uint32_t low = 0xFFFFFFFFu;
@@ -945,7 +951,7 @@ __device__ __forceinline__ bool weno_const_div_ok(const float (&v)[kAxisTaps]) {
     mag += __builtin_fabsf(v[t]);
     low = min(low, (__builtin_bit_cast(uint32_t, v[t]) << 1) - 2u);
   }
-  return mag <= 0x1p45f && low >= 2u * kLow - 2u;
+  return mag <= 0x1p27f && low >= 2u * kLow - 2u;
 }
 
 // One channel: with the FAST divisions where the range check allows them.  The
@@ -953,7 +959,7 @@ __device__ __forceinline__ bool weno_const_div_ok(const float (&v)[kAxisTaps]) {
 // compiler cannot share its subexpressions with the FAST path and hoist them
 // above the branch (which held both paths' values live: 82 VGPRs against 60).
 __device__ __forceinline__ float weno_channel(const float (&v)[kAxisTaps]) {
-  if (weno_const_div_ok(v)) return weno_norm_sq<true>(v);
+  if (weno_fast_ok(v)) return weno_norm_sq<true>(v);
   float w[kAxisTaps];
 #pragma unroll
   for (int t = 0; t < kAxisTaps; ++t) {
@@ -1013,7 +1019,7 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
         float v[S::kTaps];
 #pragma unroll
         for (int t = 0; t < S::kTaps; ++t) v[t] = v4[t][c];
-        fast = fast && weno_const_div_ok(v);
+        fast = fast && weno_fast_ok(v);
         r[c] = weno_norm_sq<true>(v);
       }
       if (!fast) {  // a value outside that range: the four channels again with IEEE divisions

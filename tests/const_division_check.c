@@ -8,8 +8,10 @@
  * remainder x - q * d (exact, a nonzero multiple of 2^(field - 153)) and the
  * result are all normal and finite, so scaling x by a power of two scales
  * every step exactly: the outcome for fields 27..254 is that of field 27 (the
- * three later fields are tried as a check of that).  The result for -x is the
- * exact negation (round-to-nearest-even is odd), so this covers every finite x.
+ * three later fields are tried as a check of that).  For nonzero x the result
+ * for -x is the exact negation (round-to-nearest-even is odd), so this covers
+ * every finite nonzero x; of the zeros, +0 is among the patterns tried and -0
+ * is tried alone: it gives +0, not the IEEE -0.
  *
  * Prints, per divisor, the number of disagreeing x tried and the exponent
  * field from which all agree; exit status 0 when both agree for zero and for
@@ -54,6 +56,9 @@ int main(void) {
     }
     printf("d=%g: %ld x disagree, all agree from exponent field %d on\n", d, bad, top_bad + 1);
     if (top_bad >= 3) status = 1;
+    const float mz = -0.0f, q0 = mz * rd, q = fmaf(fmaf(-q0, d, mz), rd, q0);
+    printf("d=%g: -0 gives %s0 (IEEE %s0)\n", d, signbit(q) ? "-" : "+", signbit(mz / d) ? "-" : "+");
+    if (signbit(q) || !signbit(mz / d)) status = 1;  /* the documented +0 */
   }
   return status;
 }

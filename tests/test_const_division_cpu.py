@@ -6,7 +6,8 @@ path only where a range check on the tap values shows every dividend to be zero
 or at least 2^-124 in magnitude and finite.  const_division_check.c compares
 the shortcut with the IEEE quotient over every fp32 dividend of the exponent
 fields that can differ (and, by exact scaling, all others); this test runs it
-and requires agreement from 2^-124 up.
+and requires agreement from 2^-124 up, and +0 for -0 (the IEEE quotient is -0;
+the kernels never pass the sign of a zero candidate on).
 """
 import os
 import re
@@ -32,3 +33,5 @@ def test_shortcut_equals_ieee_division(tmp_path):
     assert len(fields) == 2 and max(fields) <= 3, r.stdout
     # the shortcut does miss for some subnormal quotients: the check would see a broken comparison
     assert all(int(n) > 0 for n in re.findall(r": (\d+) x disagree", r.stdout)), r.stdout
+    # -0 comes out +0 (documented; the kernels never pass a zero's sign on)
+    assert r.stdout.count("-0 gives +0 (IEEE -0)") == 2, r.stdout
