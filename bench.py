@@ -76,7 +76,7 @@ def kernel_sources_sha256():
     """Hash of the kernel sources; the HBM counters in profiles/ are valid only for this hash."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("vbm_device.hpp", "vbm_kernels.hip"):
+    for f in ("vbm_device.hpp", "vbm_division.hpp", "vbm_kernels.hip"):
         with open(os.path.join(ROOT, "nanovdb_stencil_filtering_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
