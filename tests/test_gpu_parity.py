@@ -506,14 +506,19 @@ def test_filters_on_two_streams_interleaved():
 
 
 def test_graph_replays_match_the_oracle():
-    """Decode and the cached box filter captured in one HIP graph: every replay,
-    with eager work on the same buffers in between, gives the oracle's bytes."""
+    """Decode, the cached box filter (buffer-resource and 64-bit row paths) and
+    the WENO consumer captured in one HIP graph: every replay, with eager work on
+    the same buffers in between, gives the oracle's bytes."""
     g, ref = grid_pair("tiny_shell", 7)
     rl, ro = ref.decode(7)
     sc = I.sidecar(403, g.n_active, 16)
+    sc[0] = 0.25  # background of the WENO consumer
     want = ref.box(sc).view(np.uint32)
+    want_weno = ref.weno(sc).view(np.uint32)
     sct = torch.from_numpy(sc).cuda()
     out = torch.empty_like(sct)
+    out_wide = torch.empty_like(sct)
+    out_weno = torch.empty_like(sct)
     leaf = torch.empty(g.n_slots, dtype=torch.int32, device="cuda")
     off = torch.empty(g.n_slots, dtype=torch.int16, device="cuda")
     lib = vbm.load_library()
@@ -524,6 +529,8 @@ def test_graph_replays_match_the_oracle():
         assert lib.vbm_decode(ctypes.byref(g.hdr), ctypes.c_void_p(g.blob.data_ptr()),
                               ctypes.c_void_p(leaf.data_ptr()), ctypes.c_void_p(off.data_ptr()), sp) == 0
         vbm.box_filter(g, sct, vbm.CACHED | vbm.STREAMING, out=out, stream=stream)
+        vbm.box_filter(g, sct, vbm.CACHED | vbm.STREAMING | vbm.WIDE_ROWS, out=out_wide, stream=stream)
+        vbm.weno_filter(g, sct, vbm.CACHED | vbm.STREAMING, out=out_weno, stream=stream)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -536,12 +543,15 @@ def test_graph_replays_match_the_oracle():
         step(torch.cuda.current_stream())
     for k in range(3):
         say("graph replay %d" % k)
-        out.fill_(float("nan"))
+        for o in (out, out_wide, out_weno):
+            o.fill_(float("nan"))
         leaf.fill_(-1)
         off.fill_(-1)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(u32(out), want), k
+        assert np.array_equal(u32(out_wide), want), k
+        assert np.array_equal(u32(out_weno), want_weno), k
         assert np.array_equal(leaf.cpu().numpy().view(np.uint32), rl), k
         assert np.array_equal(off.cpu().numpy().view(np.uint16), ro), k
