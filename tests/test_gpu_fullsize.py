@@ -96,11 +96,19 @@ def test_cfg_shell_box_every_row(shell, C):
     sc = I.sidecar(2, N, C)   # seed 2: the benchmark's sidecar
     want = ref.box(sc).view(np.uint32)
     sct = torch.from_numpy(sc).cuda()
-    for log2w in (7, 9):
+    # every width at 1 and 16 channels (the split kernel's launch shape differs at
+    # each: 256 work-items with one, two and four tasks at W64, W128 and W256, 512
+    # work-items with four at W512)
+    for log2w in ((6, 7, 8, 9) if C in (1, 16) else (7, 9)):
         g = grids[log2w]
         for flags in FLAGS:
             compare_every_row(lambda out: vbm.box_filter(g, sct, flags, out=out), sct, want,
                               "cfg-shell box W=%d C=%d flags=%d" % (g.width, C, flags))
+    if C == 16:  # the 64-bit row path on the whole grid as well
+        for log2w in (7, 9):
+            g = grids[log2w]
+            compare_every_row(lambda out: vbm.box_filter(g, sct, vbm.CACHED | vbm.STREAMING | vbm.WIDE_ROWS, out=out),
+                              sct, want, "cfg-shell box wide rows W=%d C=16" % g.width)
 
 
 @pytest.mark.parametrize("C", [1, 8])
