@@ -126,17 +126,34 @@ def test_cfg_shell_cross_every_row(shell, C):
                                   "cfg-shell cross %s W=%d C=%d flags=%d" % (op, g.width, C, flags))
 
 
-def test_cfg_shell_axis_every_row(shell):
+@pytest.mark.parametrize("C", [8, 16])
+def test_cfg_shell_axis_every_row(shell, C):
+    """C = 16 takes the split 7-direction kernel (four work-items per row)."""
     ref, grids = shell
     N = grids[7].n_active
-    sc = I.sidecar(4, N, 8)
+    sc = I.sidecar(4, N, C)
     sct = torch.from_numpy(sc).cuda()
     want = ref.axis(sc).view(np.uint32)
     for log2w in (7, 9):
         g = grids[log2w]
         for flags in FLAGS:
             compare_every_row(lambda out: vbm.axis_filter(g, sct, flags, out=out), sct, want,
-                              "cfg-shell axis W=%d C=8 flags=%d" % (g.width, flags))
+                              "cfg-shell axis W=%d C=%d flags=%d" % (g.width, C, flags))
+
+
+def test_cfg_shell_cross_split_every_row(shell):
+    """The cross sum and the Laplacian at C = 16 (the split 7-direction kernel)."""
+    ref, grids = shell
+    N = grids[7].n_active
+    sc = I.sidecar(3, N, 16)
+    sct = torch.from_numpy(sc).cuda()
+    for op, code in (("sum", vbm.OP_SUM), ("laplacian", vbm.OP_LAPLACIAN)):
+        want = ref.cross(sc, op).view(np.uint32)
+        for log2w in (7, 9):
+            g = grids[log2w]
+            for flags in FLAGS:
+                compare_every_row(lambda out: vbm.cross_filter(g, sct, flags | code, out=out), sct, want,
+                                  "cfg-shell cross %s W=%d C=16 flags=%d" % (op, g.width, flags))
 
 
 @pytest.mark.parametrize("C", [1, 4])
