@@ -186,6 +186,29 @@ def test_decode_stress_full():
             assert np.array_equal(off.cpu().numpy().view(np.uint16), ro), (log2w, sweep)
 
 
+def test_decode_stress_box_every_row():
+    """The box filter on the whole decode-stress topology (4.09M voxels in 20,000
+    leaves of 2 to 100 % occupancy): blocks spanning up to 15 leaves, so the
+    cached kernels stage their bricks in several passes (3 leaves per pass at
+    W128, 8 at W512); every row against the oracle at C = 1 and 16, all flags."""
+    coords = I.leaf_bernoulli_coords(4, **I.STRESS)
+    ref = oracle.OracleGrid(coords)
+    grids = {w: vbm.build(coords, w) for w in (7, 9)}
+    for w, cap in ((7, 3), (9, 8)):  # blocks that need more than one brick pass exist
+        jump = ref.blocks(w)["jump"]
+        span = 1 + np.unpackbits(jump.view(np.uint8), axis=1).sum(axis=1)
+        assert span.max() > cap and span.max() <= vbm.MAX_CACHED_LEAVES, (w, int(span.max()))
+    for C in (1, 16):
+        sc = I.sidecar(7, ref.n_active, C)
+        want = ref.box(sc).view(np.uint32)
+        sct = torch.from_numpy(sc).cuda()
+        for log2w, g in grids.items():
+            for flags in FLAGS:
+                compare_every_row(lambda out: vbm.box_filter(g, sct, flags, out=out), sct, want,
+                                  "stress box W=%d C=%d flags=%d" % (g.width, C, flags))
+        del sct
+
+
 def tree_keys(c):
     """One int64 per coordinate, ordered as the index grid orders voxels: root
     tile (p >> 12, signed), upper-node slot, lower-node slot, voxel offset."""
