@@ -209,6 +209,30 @@ def test_decode_stress_box_every_row():
         del sct
 
 
+def test_sparse_fallback_every_row():
+    """One voxel in each 8^3 cell of a 48^3 lattice (110,592 voxels, each its own
+    leaf): every block spans W > 16 leaves, so the cached kernels take their
+    tree-walk fallback in every block, with more than 512 blocks (the 8-channel
+    stencil kernels' touch-ahead path); every row against the oracle."""
+    coords = I.one_per_cell_coords(9, 48)
+    ref = oracle.OracleGrid(coords)
+    assert ref.n_leaves == ref.n_active == 48 ** 3
+    for log2w in (7, 9):
+        g = vbm.build(coords, log2w)
+        for C in (1, 8, 16):
+            sc = I.sidecar(8, ref.n_active, C)
+            sct = torch.from_numpy(sc).cuda()
+            want = ref.box(sc).view(np.uint32)
+            for flags in FLAGS:
+                compare_every_row(lambda out: vbm.box_filter(g, sct, flags, out=out), sct, want,
+                                  "sparse box W=%d C=%d flags=%d" % (g.width, C, flags))
+            if C == 8:
+                want = ref.cross(sc, "laplacian").view(np.uint32)
+                for flags in FLAGS:
+                    compare_every_row(lambda out: vbm.cross_filter(g, sct, flags | vbm.OP_LAPLACIAN, out=out), sct,
+                                      want, "sparse laplacian W=%d C=8 flags=%d" % (g.width, flags))
+
+
 def tree_keys(c):
     """One int64 per coordinate, ordered as the index grid orders voxels: root
     tile (p >> 12, signed), upper-node slot, lower-node slot, voxel offset."""
