@@ -106,12 +106,6 @@ struct WideSidecar {
   }
 };
 
-__device__ __forceinline__ Sidecar make_sidecar(const float* sc, uint32_t bytes, uint32_t C, uint32_t ch0) {
-  return Sidecar::make(sc, bytes, C, ch0);
-}
-
-__device__ __forceinline__ uint32_t tap_offset(const Sidecar& s, uint32_t idx) { return s.tap(idx); }
-
 // acc[c] += row[c] for the CH channels of handle h (an inactive tap: zeros),
 // from byte in_row of the row on.
 template <int CH, bool VEC, class SC>
