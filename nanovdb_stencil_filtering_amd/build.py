@@ -4,10 +4,11 @@ hipcc compiles the kernels and the C-ABI launchers (vbm_kernels.hip) and the
 device-side grid build (vbm_build_device.hip) in parallel; g++ compiles the
 host grid builder (vbm_build.cpp); hipcc links them into
 nanovdb_stencil_filtering_amd/_lib/libvbm.so.  Kernel resource usage (VGPRs,
-SGPRs, scratch, LDS, occupancy) is written to _lib/resource_usage.txt.  Two
+SGPRs, scratch, LDS, occupancy) is written to _lib/resource_usage.txt.  Three
 libraries for the tests are built beside it: libvbm_poison.so (the same
-library with every brick cell poisoned before each brick pass) and
-libvbm_divcheck.so (the GPU check of the WENO kernels' shortcut divisions).
+library with every brick cell poisoned before each brick pass),
+libvbm_divcheck.so (the GPU check of the WENO kernels' shortcut divisions) and
+libvbm_example.so (a consumer written on the device header alone).
 """
 from __future__ import annotations
 
@@ -26,6 +27,9 @@ POISON_LIB = os.path.join(LIBDIR, "libvbm_poison.so")
 # GPU check of the WENO kernels' shortcut divisions (tests/division_check.hip)
 DIVCHECK_LIB = os.path.join(LIBDIR, "libvbm_divcheck.so")
 DIVCHECK_SRC = os.path.join(ROOT, "tests", "division_check.hip")
+# a consumer written on the device header alone (tests/custom_consumer.hip)
+EXAMPLE_LIB = os.path.join(LIBDIR, "libvbm_example.so")
+EXAMPLE_SRC = os.path.join(ROOT, "tests", "custom_consumer.hip")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -81,11 +85,14 @@ def build() -> str:
             _start([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "vbm_build_device.hip"), "-o", d_obj],
                    os.path.join(LIBDIR, "resource_usage_build_device.txt")),
             _start([HIPCC, *HIP_FLAGS, "-shared", DIVCHECK_SRC, "-o", DIVCHECK_LIB + ".tmp%d" % os.getpid()],
-                   os.path.join(LIBDIR, "divcheck_build.txt"))]
+                   os.path.join(LIBDIR, "divcheck_build.txt")),
+            _start([HIPCC, *HIP_FLAGS, "-shared", EXAMPLE_SRC, "-o", EXAMPLE_LIB + ".tmp%d" % os.getpid()],
+                   os.path.join(LIBDIR, "example_build.txt"))]
     _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "vbm_build.cpp"), "-o", b_obj])
     for j in jobs:
         _finish(j)
     os.replace(DIVCHECK_LIB + ".tmp%d" % os.getpid(), DIVCHECK_LIB)
+    os.replace(EXAMPLE_LIB + ".tmp%d" % os.getpid(), EXAMPLE_LIB)
     for lib, objs in ((LIB, [k_obj, d_obj, b_obj]), (POISON_LIB, [p_obj, d_obj, b_obj])):
         tmp = lib + ".tmp%d" % os.getpid()
         _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])

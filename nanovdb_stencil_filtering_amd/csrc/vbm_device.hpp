@@ -1,7 +1,8 @@
 // Device-side building blocks of the VBM stencil pipeline for gfx950.
 //
 // Header-only, so custom consumers can be written as HIP kernels on top of
-// the same decode and resolvers:
+// the same decode and resolvers (tests/custom_consumer.hip is one):
+//   device_grid_of         the device view of a grid (header + device blob)
 //   decode_slot            slot -> (leaf, voxel offset); thread-local, in registers
 //   resolve_tree           one tap by a root-down tree walk
 //   stage_neighbour_table  per-block LDS table of neighbour leaf ids (all threads)
@@ -29,6 +30,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "vbm.h"
 
 namespace vbm {
 
@@ -68,6 +71,24 @@ struct DeviceGrid {
   uint32_t n_blocks;
   int32_t log2w;
 };
+
+// The device view of a grid: the header from vbm_build (or the device build)
+// and the device copy of its blob.  Host or device code.
+__host__ __device__ inline DeviceGrid device_grid_of(const vbm_grid& hdr, const void* d_blob) {
+  const uint8_t* base = static_cast<const uint8_t*>(d_blob);
+  DeviceGrid g;
+  g.leaves = reinterpret_cast<const Leaf*>(base + hdr.off_leaves);
+  g.root = reinterpret_cast<const RootTile*>(base + hdr.off_root);
+  g.upper = reinterpret_cast<const uint32_t*>(base + hdr.off_upper);
+  g.lower = reinterpret_cast<const uint32_t*>(base + hdr.off_lower);
+  g.block_first_leaf = reinterpret_cast<const uint32_t*>(base + hdr.off_block_first_leaf);
+  g.block_jump = reinterpret_cast<const uint64_t*>(base + hdr.off_block_jump);
+  g.n_active = uint32_t(hdr.n_active);
+  g.n_root = hdr.n_root;
+  g.n_blocks = hdr.n_blocks;
+  g.log2w = hdr.log2_width;
+  return g;
+}
 
 struct Slot {
   uint32_t leaf;    // kSentinelLeaf past the last active index

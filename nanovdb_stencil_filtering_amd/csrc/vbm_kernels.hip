@@ -1241,21 +1241,7 @@ int check_grid(const vbm_grid* grid, const void* d_blob) {
   return VBM_OK;
 }
 
-DeviceGrid device_grid(const vbm_grid* grid, const void* d_blob) {
-  const uint8_t* base = static_cast<const uint8_t*>(d_blob);
-  DeviceGrid g;
-  g.leaves = reinterpret_cast<const Leaf*>(base + grid->off_leaves);
-  g.root = reinterpret_cast<const RootTile*>(base + grid->off_root);
-  g.upper = reinterpret_cast<const uint32_t*>(base + grid->off_upper);
-  g.lower = reinterpret_cast<const uint32_t*>(base + grid->off_lower);
-  g.block_first_leaf = reinterpret_cast<const uint32_t*>(base + grid->off_block_first_leaf);
-  g.block_jump = reinterpret_cast<const uint64_t*>(base + grid->off_block_jump);
-  g.n_active = uint32_t(grid->n_active);
-  g.n_root = grid->n_root;
-  g.n_blocks = grid->n_blocks;
-  g.log2w = grid->log2_width;
-  return g;
-}
+DeviceGrid device_grid(const vbm_grid* grid, const void* d_blob) { return device_grid_of(*grid, d_blob); }
 
 using vbm_host::check_kernel_memory;
 using vbm_host::launch_status;
