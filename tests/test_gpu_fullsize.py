@@ -13,9 +13,12 @@ benchmark times (no CPU fallback: every output comes from the HIP path).
 * decode stress (20,000 random leaves, Bernoulli masks): full decode maps,
   select and sweep, every width, against the oracle, partial last block and
   sentinels included;
-* noisy narrow band (R=600, |d| <= 3, ~27M voxels), cached streaming box at
-  W512, C=16: the oracle's hash map is too large to build here, so sampled
-  rows are checked through a property that holds at any size: with an integer
+* noisy narrow band (R=600, |d| <= 3, 26.8M voxels), box filter at C=16 with
+  the workload's own sidecar (uniform [-1, 1], the benchmark's seed): every row
+  of all four resolver / delivery flags at W512 and of the cached streaming
+  box at W128 against the oracle's whole-band result (about a minute of CPU
+  and 18 GB of host memory for the oracle); and, independent of the oracle,
+  sampled rows through a property that holds at any size: with an integer
   field of magnitude < 2^11 every partial sum is exact in fp32, so each output
   must equal the exact sum of the field over the voxel's active 3x3x3
   neighbourhood, whose members come from the coordinate set alone (sorted
@@ -255,10 +258,36 @@ def integer_field(c, channels):
     return out
 
 
-def test_band_box_w512_c16_integer_field():
+@pytest.fixture(scope="module")
+def band_coords():
     say("band: generating coordinates")
     coords = I.band_coords(5, **I.BAND)
     assert abs(coords.shape[0] - 26.8e6) < 1e6
+    return coords
+
+
+def test_band_box_every_row(band_coords):
+    say("band: oracle grid")
+    ref = oracle.OracleGrid(band_coords)
+    N = ref.n_active
+    C = 16
+    sc = I.sidecar(6, N, C)  # seed 6: the benchmark's band sidecar
+    say("band: oracle box filter, N=%d C=%d" % (N, C))
+    want = ref.box(sc).view(np.uint32)
+    del ref
+    sct = torch.from_numpy(sc).cuda()
+    del sc
+    for log2w, flag_set in ((9, FLAGS), (7, [CS])):
+        g = vbm.build(band_coords, log2w)
+        assert g.n_active == N
+        for flags in flag_set:
+            compare_every_row(lambda out: vbm.box_filter(g, sct, flags, out=out), sct, want,
+                              "band box W=%d C=%d flags=%d" % (g.width, C, flags))
+        del g
+
+
+def test_band_box_w512_c16_integer_field(band_coords):
+    coords = band_coords
     keys = tree_keys(coords)
     order = np.argsort(keys, kind="stable")
     sorted_keys = keys[order]
