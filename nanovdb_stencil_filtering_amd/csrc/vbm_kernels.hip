@@ -200,31 +200,36 @@ __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t
   }
 }
 
-// Loads the rows of block bn (indices 1 + bn*W .. (bn+1)*W, one contiguous byte
-// range of the sidecar) as 16-byte pieces, piece threadIdx.x + k * blockDim.x in
-// v[k], so that a later block finds its rows in the L2.  The caller consumes v
+// Prefetch of block bn's rows (indices 1 + bn*W .. (bn+1)*W, one contiguous byte
+// range of the sidecar) into the L2, so that a later block finds them there: one
+// dword of each 128-byte line of the range (the L2 fetches whole lines), line
+// threadIdx.x + k * blockDim.x in v[k], so the first N * blockDim.x lines.  A
+// dword per line takes a small fraction of the address cycles that loading the
+// rows themselves took, and leaves the L1 to the gather.  The caller consumes v
 // only at its very end (consume_touch), so no wave waits for these loads.
 // bn = 0xFFFFFFFF (or a block past the grid) loads nothing.
 template <int N, class SC>
-__device__ __forceinline__ void touch_block_rows(const DeviceGrid& g, const SC& side, uint32_t bn, f32x4 (&v)[N]) {
-  if constexpr (SC::kWide) {  // the wide path does not prefetch
+__device__ __forceinline__ void touch_block_lines(const DeviceGrid& g, const SC& side, uint32_t bn, float (&v)[N]) {
 #pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  } else {
+  for (int k = 0; k < N; ++k) v[k] = 0.0f;
+  if constexpr (!SC::kWide) {  // the wide path does not prefetch
     const bool has = bn < g.n_blocks;
     const uint64_t row0 = 1 + (uint64_t(has ? bn : 0u) << g.log2w);
     const uint64_t rows = has ? min(uint64_t(1) << g.log2w, uint64_t(g.n_active) + 1 - row0) : 0;
-    const uint32_t pieces = uint32_t((rows * side.row_bytes + 15) / 16);
+    const uint64_t begin = row0 * side.row_bytes & ~uint64_t(127);  // the line holding the first row
+    const uint64_t end = (row0 + rows) * side.row_bytes;
+    const uint32_t lines = rows ? uint32_t((end - begin + 127) / 128) : 0u;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const uint32_t piece = threadIdx.x + k * blockDim.x;
-      const uint32_t off = piece < pieces ? uint32_t(row0) * side.row_bytes + 16 * piece : kInactive;
-      v[k] = side.load4(off, 0);
+      if (k == 0 || k * blockDim.x < lines) {  // workgroup-uniform
+        const uint32_t line = threadIdx.x + k * blockDim.x;
+        v[k] = side.load1(line < lines ? uint32_t(begin + uint64_t(line) * 128) : kInactive, 0);
+      }
     }
   }
 }
 template <int N>
-__device__ __forceinline__ void consume_touch(const f32x4 (&v)[N]) {
+__device__ __forceinline__ void consume_touch(const float (&v)[N]) {
 #pragma unroll
   for (int k = 0; k < N; ++k) asm volatile("" :: "v"(v[k]));
 }
@@ -571,30 +576,6 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   if (b >= g.n_blocks) return;  // padding workgroup
   if (blockIdx.x == 0 && threadIdx.x < CH) out[ch0 + threadIdx.x] = 0.0f;
   const SC side = SC::make(sc, sc_bytes, C, ch0);
-  // Touch the own rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks
-  // later (about two per CU), so that block finds them in the L2 instead of HBM;
-  // near enough that they are still in the 4 MB L2 when it starts, far enough
-  // that the loads have landed.  The values are consumed only at the very end
-  // (no wave waits for them).
-  f32x4 ahead[2];
-  {
-    const uint32_t per = (g.n_blocks + 7) / 8;
-    const uint32_t in_xcd = b - (blockIdx.x % 8) * per;
-    const bool has = VBM_PREFETCH_AHEAD > 0 && in_xcd + VBM_PREFETCH_AHEAD < per;
-    const uint32_t bn = b + VBM_PREFETCH_AHEAD;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t piece = threadIdx.x + k * blockDim.x;  // 16-byte pieces of the block's W rows
-      const uint64_t row = 1 + (uint64_t(bn) << g.log2w) + piece / LANES;
-      if constexpr (SC::kWide) {  // the wide path does not prefetch
-        ahead[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      } else {
-        const uint32_t off = has && piece < W * LANES && row <= g.n_active
-                                 ? uint32_t(row) * side.row_bytes + 16 * (piece % LANES) : kInactive;
-        ahead[k] = side.load4(off, 0);
-      }
-    }
-  }
   const uint32_t first = g.block_first_leaf[b];
   const uint32_t span = block_span(g, b);  // block-uniform: every barrier below is uniform
   const uint32_t tasks = W * LANES;
@@ -636,6 +617,19 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
   if (blockDim.x == W || threadIdx.x >= W) fill_table_range(g, first, count0, table, stager, stagers);
 #endif
   __syncthreads();
+  // Prefetch the rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks
+  // later (about two per CU), so that block finds them in the L2 instead of HBM;
+  // near enough that they are still in the 4 MB L2 when it starts, far enough
+  // that the loads have landed.  Issued after the decode and the table: vector
+  // loads retire in order, so a prefetch issued earlier would hold up the waits
+  // of the decode's own loads behind its trip to HBM.
+  float ahead[1];  // one line per work-item: the whole block at up to 32 channels
+  {
+    const uint32_t per = (g.n_blocks + 7) / 8;
+    const uint32_t in_xcd = b - (blockIdx.x % 8) * per;
+    const bool has = VBM_PREFETCH_AHEAD > 0 && in_xcd + VBM_PREFETCH_AHEAD < per;
+    touch_block_lines(g, side, has ? b + VBM_PREFETCH_AHEAD : 0xFFFFFFFFu, ahead);
+  }
   if (!cached) {  // per-tap tree walk
     for (uint32_t task = threadIdx.x; task < tasks; task += blockDim.x) {
       const uint32_t info = slot_corner[task / LANES];
@@ -682,7 +676,7 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       }
     }
   }
-  asm volatile("" :: "v"(ahead[0]), "v"(ahead[1]));  // keeps the touch loads
+  consume_touch(ahead);
 }
 
 // Filters of the 7-direction shapes: the cross (sum, or 7-point Laplacian =
@@ -713,10 +707,10 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
   // round-robin over the 8 XCDs here, hence the factor 8).  Measured on MI355X:
   // 3-6 % faster at 8 channels a work-item, 2-3 % slower at 1, so only the wide form.
   constexpr bool kTouch = CH >= 8;
-  f32x4 ahead[kTouch ? (CH + 3) / 4 : 1];
+  float ahead[1];  // one line per work-item: the whole block at up to 32 channels
   if constexpr (kTouch)
-    touch_block_rows(g, side, VBM_PREFETCH_AHEAD && b + 8 * VBM_PREFETCH_AHEAD < g.n_blocks
-                                  ? b + 8 * VBM_PREFETCH_AHEAD : 0xFFFFFFFFu, ahead);
+    touch_block_lines(g, side, VBM_PREFETCH_AHEAD && b + 8 * VBM_PREFETCH_AHEAD < g.n_blocks
+                                   ? b + 8 * VBM_PREFETCH_AHEAD : 0xFFFFFFFFu, ahead);
   if (!valid) {
     if constexpr (kTouch) consume_touch(ahead);
     return;

@@ -56,7 +56,8 @@ def test_kernels_present(device_asm):
 def test_vector_sidecar_loads_are_16_bytes(device_asm):
     """The float4 path must load 16 bytes per instruction (an element-wise
     extraction of the buffer-load vector once collapsed into one dword load
-    reused for all four channels)."""
+    reused for all four channels).  The one dword load the split kernel may
+    hold is its L2 prefetch of a later block (one dword per 128-byte line)."""
     for name, body in kernels(device_asm):
         if "k_box" in name and "ILi16ELb1E" in name and "WideSidecar" in name:
             # rows by 64-bit addresses: 16-byte global loads, no buffer resource at all
@@ -64,4 +65,5 @@ def test_vector_sidecar_loads_are_16_bytes(device_asm):
             assert "buffer_load" not in body, name
         elif "k_box" in name and "ILi16ELb1E" in name:
             assert "buffer_load_dwordx4" in body, name
-            assert "buffer_load_dword " not in body.replace("buffer_load_dwordx4", ""), name
+            dword = body.replace("buffer_load_dwordx4", "").count("buffer_load_dword ")
+            assert dword <= (1 if "k_box_cached_split" in name else 0), (name, dword)
