@@ -34,7 +34,9 @@
  *     launch is reported as VBM_ERR_HIP.
  *   - Device buffers are owned by the caller.  The library allocates no device
  *     memory and keeps no state between calls (the device-side build passes its
- *     state from plan to fill in the caller's workspace).
+ *     state from plan to fill in the caller's workspace).  The one exception is
+ *     vbm_build_device_static below, whose workspace is a static array of the
+ *     library on each GPU it runs on.
  *   - Coordinates x -> di, y -> dj, z -> dk.  Leaves are 8^3; the voxel offset
  *     inside a leaf is o = (x&7)*64 + (y&7)*8 + (z&7).
  */
