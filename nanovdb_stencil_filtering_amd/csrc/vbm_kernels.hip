@@ -806,12 +806,44 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
     if (info == 0xFFFFFFFFu) continue;
     const uint32_t q = task % LANES, j = info >> 16, o = info & 0xFFFF;
     const int x = int(o >> 6), y = int((o >> 3) & 7), z = int(o & 7);
-    // index of tap t ((LAP) the centre reads as inactive: it enters only as -6 * centre)
+    // The four tasks of a slot are the four lanes of one quad (task = 4 slot + q
+    // with 64-lane waves of consecutive tasks), so the slot's taps are resolved
+    // once, not four times: lane q resolves taps q, q + 4, q + 8, ... (by the
+    // staged records or a tree walk) and tap t is read from lane t % 4 of the
+    // quad by a quad-permute DPP move.  A quad is active or idle as a whole (a
+    // sentinel slot skips all four of its tasks), so every lane a DPP move reads
+    // is active.  ((LAP) the centre reads as inactive: it enters only as -6 * centre.)
+    static_assert(LANES == 4, "taps are shared within quads");
+    constexpr int kPer = (S::kTaps + 3) / 4;
+    uint32_t mine[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      // offset of this lane's tap 4 r + q, chosen among four constants
+      auto pick = [&](auto f) {
+        const int a = f(4 * r), b = f(4 * r + 1), c = f(4 * r + 2), d = f(4 * r + 3);
+        return q == 0 ? a : q == 1 ? b : q == 2 ? c : d;
+      };
+      const int di = pick([](int t) { return t < S::kTaps ? S::di(t) : 0; });
+      const int dj = pick([](int t) { return t < S::kTaps ? S::dj(t) : 0; });
+      const int dk = pick([](int t) { return t < S::kTaps ? S::dk(t) : 0; });
+      const int t = 4 * r + int(q);
+      if (t >= S::kTaps || (LAP && t == S::kCentre)) {
+        mine[r] = 0u;
+      } else if (cached) {
+        mine[r] = resolve_staged<S::kDirs>(staged, j, x, y, z, di, dj, dk);
+      } else {
+        const Leaf& L = g.leaves[first + j];
+        mine[r] = resolve_tree(g, L.origin[0] + x + di, L.origin[1] + y + dj, L.origin[2] + z + dk);
+      }
+    }
     auto tap = [&](int t) -> uint32_t {
-      if (LAP && t == S::kCentre) return 0u;
-      if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t));
-      const Leaf& L = g.leaves[first + j];
-      return resolve_tree(g, L.origin[0] + x + S::di(t), L.origin[1] + y + S::dj(t), L.origin[2] + z + S::dk(t));
+      const int v = int(mine[t / 4]);
+      switch (t % 4) {  // broadcast of lane t % 4 of the quad (t is a constant once unrolled)
+        case 0: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
+        case 1: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
+        case 2: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
+        default: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
+      }
     };
     // bytes 16 q .. 16 q + 15 of each tap's row
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
