@@ -300,6 +300,7 @@ __host__ __device__ constexpr int axis_dk(int j) { return (j >= 6 && j < 13) ? j
 // Stencil shapes: tap count, cached-table directions per leaf, offsets.
 struct BoxShape {
   static constexpr int kTaps = kBoxTaps, kDirs = 27;
+  static constexpr int kCentre = 13;
   __host__ __device__ static constexpr int di(int t) { return box_di(t); }
   __host__ __device__ static constexpr int dj(int t) { return box_dj(t); }
   __host__ __device__ static constexpr int dk(int t) { return box_dk(t); }

@@ -262,6 +262,9 @@ __device__ __forceinline__ void consume_touch(const float (&v)[N]) {
 #ifndef VBM_PREFETCH_AHEAD
 #define VBM_PREFETCH_AHEAD 64  // split box, split cross, 8-channel stencils: blocks ahead (per XCD) whose rows each workgroup prefetches; 0 = off
 #endif
+#ifndef VBM_PLAIN_SPLIT
+#define VBM_PLAIN_SPLIT 1  // 16-channel tree-walk box: rows split over quads, taps walked once per slot
+#endif
 #ifndef VBM_STAGE_LEAVES
 #define VBM_STAGE_LEAVES 1  // 1: the split-row kernel stages neighbour leaf records in LDS for the brick build
 #endif
@@ -1361,6 +1364,13 @@ struct BoxLauncher {
       const uint32_t cap = brick_capacity(g.log2w);
       hipLaunchKernelGGL((k_box_cached<CH, VEC, STREAM>), dim3(box_grid_size(g.n_blocks)), dim3(1u << g.log2w),
                          brick_lds_bytes(cap), st, g, sc, bytes, out, C, ch0, cap);
+    } else if constexpr (VBM_PLAIN_SPLIT && VEC && CH == 16) {
+      // tree walk with the rows split over quads: the split 7-direction kernel on
+      // the box shape, no table (each tap walked once per slot, shared in the quad)
+      const uint32_t W = 1u << g.log2w, tasks = W * (CH / 4);
+      const uint32_t threads = tasks < 256 ? tasks : (W > 256 ? W : 256u);
+      hipLaunchKernelGGL((k_stencil_split<BoxShape, CH, false, false, STREAM>), dim3(box_grid_size(g.n_blocks)),
+                         dim3(threads), 0, st, g, sc, bytes, out, C, ch0);
     } else {
       hipLaunchKernelGGL((k_box_plain<CH, VEC, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st, g, sc,
                          bytes, out, C, ch0);
@@ -1375,7 +1385,7 @@ struct StencilLauncher {
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
     using SC = std::conditional_t<WIDE, WideSidecar, Sidecar>;
-    if constexpr (VBM_STENCIL_SPLIT && VEC && CH == 16) {  // at CH = 8 one work-item per row is faster
+    if constexpr (VBM_STENCIL_SPLIT && VEC && CH == 16) {  // at CH = 8 one work-item per row is as fast or faster
       const uint32_t W = 1u << g.log2w, tasks = W * (CH / 4);
       const uint32_t threads = tasks < 256 ? tasks : (W > 256 ? W : 256u);
       hipLaunchKernelGGL((k_stencil_split<S, CH, CACHED, LAP, STREAM, SC>), dim3(box_grid_size(g.n_blocks)),
