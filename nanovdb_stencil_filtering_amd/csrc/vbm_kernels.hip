@@ -192,6 +192,55 @@ __device__ __forceinline__ void store_row(float* __restrict__ p, const float (&a
   }
 }
 
+// The taps of one slot shared by its LANES work-items of a split kernel (LANES
+// adjacent lanes of one quad, 2 or 4; task = LANES slot + q with 64-lane waves
+// of consecutive tasks): lane q resolves taps q, q + LANES, ... once, and tap t
+// is read from lane t % LANES of the slot by a quad-permute DPP move, instead
+// of every lane resolving every tap.  Every lane a move reads must be active:
+// callers keep a slot's lanes active or idle together.
+template <int LANES, class S>
+struct SlotTaps {
+  static_assert(LANES == 2 || LANES == 4, "taps are shared within pairs or quads");
+  static constexpr int kPer = (S::kTaps + LANES - 1) / LANES;
+  uint32_t mine[kPer];
+  // res(t, di, dj, dk): index of tap t (< S::kTaps) at offset (di, dj, dk)
+  template <class Resolve>
+  __device__ __forceinline__ void resolve(uint32_t q, Resolve&& res) {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      auto pick = [&](auto f) {  // the offset of tap LANES r + q, chosen among LANES constants
+        const int a = f(LANES * r), b = f(LANES * r + 1);
+        if constexpr (LANES == 2) {
+          return q == 0 ? a : b;
+        } else {
+          const int c = f(LANES * r + 2), d = f(LANES * r + 3);
+          return q == 0 ? a : q == 1 ? b : q == 2 ? c : d;
+        }
+      };
+      const int di = pick([](int t) { return t < S::kTaps ? S::di(t) : 0; });
+      const int dj = pick([](int t) { return t < S::kTaps ? S::dj(t) : 0; });
+      const int dk = pick([](int t) { return t < S::kTaps ? S::dk(t) : 0; });
+      const int t = LANES * r + int(q);
+      mine[r] = t < S::kTaps ? res(t, di, dj, dk) : 0u;
+    }
+  }
+  // tap t (a constant once the caller's loop is unrolled)
+  __device__ __forceinline__ uint32_t operator()(int t) const {
+    const int v = int(mine[t / LANES]);
+    if constexpr (LANES == 2) {  // lane t % 2 of each pair: quad_perm [0,0,2,2] or [1,1,3,3]
+      if (t % 2 == 0) return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xA0, 0xF, 0xF, false));
+      return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xF5, 0xF, 0xF, false));
+    } else {
+      switch (t % 4) {  // lane t % 4 of the quad
+        case 0: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
+        case 1: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
+        case 2: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
+        default: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
+      }
+    }
+  }
+};
+
 template <int CH>
 __device__ __forceinline__ void zero_index_row(float* __restrict__ out, uint32_t ch0) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -641,7 +690,9 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
       const uint32_t cell = info & 0xFFFF;
       const int x = L.origin[0] + int(cell / 100), y = L.origin[1] + int((cell / 10) % 10);
       const int z = L.origin[2] + int(cell % 10);
-      run(task, [&](int t) { return side.tap(resolve_tree(g, x + box_di(t), y + box_dj(t), z + box_dk(t))); });
+      SlotTaps<LANES, BoxShape> taps;  // each tap walked once per slot, shared by its LANES work-items
+      taps.resolve(task % LANES, [&](int, int di, int dj, int dk) { return resolve_tree(g, x + di, y + dj, z + dk); });
+      run(task, [&](int t) { return side.tap(taps(t)); });
     }
     return;
   }
@@ -809,45 +860,16 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
     if (info == 0xFFFFFFFFu) continue;
     const uint32_t q = task % LANES, j = info >> 16, o = info & 0xFFFF;
     const int x = int(o >> 6), y = int((o >> 3) & 7), z = int(o & 7);
-    // The four tasks of a slot are the four lanes of one quad (task = 4 slot + q
-    // with 64-lane waves of consecutive tasks), so the slot's taps are resolved
-    // once, not four times: lane q resolves taps q, q + 4, q + 8, ... (by the
-    // staged records or a tree walk) and tap t is read from lane t % 4 of the
-    // quad by a quad-permute DPP move.  A quad is active or idle as a whole (a
-    // sentinel slot skips all four of its tasks), so every lane a DPP move reads
-    // is active.  ((LAP) the centre reads as inactive: it enters only as -6 * centre.)
-    static_assert(LANES == 4, "taps are shared within quads");
-    constexpr int kPer = (S::kTaps + 3) / 4;
-    uint32_t mine[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      // offset of this lane's tap 4 r + q, chosen among four constants
-      auto pick = [&](auto f) {
-        const int a = f(4 * r), b = f(4 * r + 1), c = f(4 * r + 2), d = f(4 * r + 3);
-        return q == 0 ? a : q == 1 ? b : q == 2 ? c : d;
-      };
-      const int di = pick([](int t) { return t < S::kTaps ? S::di(t) : 0; });
-      const int dj = pick([](int t) { return t < S::kTaps ? S::dj(t) : 0; });
-      const int dk = pick([](int t) { return t < S::kTaps ? S::dk(t) : 0; });
-      const int t = 4 * r + int(q);
-      if (t >= S::kTaps || (LAP && t == S::kCentre)) {
-        mine[r] = 0u;
-      } else if (cached) {
-        mine[r] = resolve_staged<S::kDirs>(staged, j, x, y, z, di, dj, dk);
-      } else {
-        const Leaf& L = g.leaves[first + j];
-        mine[r] = resolve_tree(g, L.origin[0] + x + di, L.origin[1] + y + dj, L.origin[2] + z + dk);
-      }
-    }
-    auto tap = [&](int t) -> uint32_t {
-      const int v = int(mine[t / 4]);
-      switch (t % 4) {  // broadcast of lane t % 4 of the quad (t is a constant once unrolled)
-        case 0: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
-        case 1: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
-        case 2: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
-        default: return uint32_t(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
-      }
-    };
+    // each tap resolved once per slot and shared in the quad ((LAP) the centre
+    // reads as inactive: it enters only as -6 * centre)
+    SlotTaps<LANES, S> taps;
+    taps.resolve(q, [&](int t, int di, int dj, int dk) -> uint32_t {
+      if (LAP && t == S::kCentre) return 0u;
+      if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, di, dj, dk);
+      const Leaf& L = g.leaves[first + j];
+      return resolve_tree(g, L.origin[0] + x + di, L.origin[1] + y + dj, L.origin[2] + z + dk);
+    });
+    auto tap = [&](int t) -> uint32_t { return taps(t); };
     // bytes 16 q .. 16 q + 15 of each tap's row
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (STREAM) {
