@@ -782,11 +782,26 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
         return side.tap(resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
       });
     } else {
+      // tree walks streamed in three groups (as in the plain box): a group's walks
+      // are independent chains of dependent loads that overlap one another, and
+      // no walk waits behind a sidecar row load (vector loads retire in order)
+      // except at a group's start; at most a third of the taps are held
       const VoxelCoord p = voxel_coord(g, s);
-      gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
-        if (LAP && t == S::kCentre) return side.inactive();
-        return side.tap(resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
-      });
+      constexpr int kG = (S::kTaps + 2) / 3;
+      auto group = [&](auto first_c, auto n_c) {
+        constexpr int F = decltype(first_c)::value, N = decltype(n_c)::value;
+        uint32_t off[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          const int t = F + k;
+          off[k] = (LAP && t == S::kCentre) ? side.inactive()
+                                            : side.tap(resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+        }
+        gather_box_pipelined<CH, VEC, (kPipe < N ? kPipe : N), N>(acc, side, [&](int k) { return off[k]; });
+      };
+      group(std::integral_constant<int, 0>{}, std::integral_constant<int, kG>{});
+      group(std::integral_constant<int, kG>{}, std::integral_constant<int, kG>{});
+      group(std::integral_constant<int, 2 * kG>{}, std::integral_constant<int, S::kTaps - 2 * kG>{});
     }
   } else {
     uint64_t st[S::kTaps];
@@ -1100,11 +1115,14 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
       for (int t = 0; t < S::kTaps; ++t)
         v4[t] = side.load4(row[t], 16 * q);
     };
-    if constexpr (STREAM) {  // first chunk: each tap resolved as its load is issued
+    if constexpr (STREAM) {  // first chunk: taps resolved and loaded in three groups (see k_stencil)
 #pragma unroll
-      for (int t = 0; t < S::kTaps; ++t) {
-        row[t] = side.row(resolve(t));
-        v4[t] = side.load4(row[t], 0);
+      for (int grp = 0; grp < 3; ++grp) {
+        constexpr int kG = (S::kTaps + 2) / 3;
+#pragma unroll
+        for (int t = grp * kG; t < (grp + 1) * kG && t < S::kTaps; ++t) row[t] = side.row(resolve(t));
+#pragma unroll
+        for (int t = grp * kG; t < (grp + 1) * kG && t < S::kTaps; ++t) v4[t] = side.load4(row[t], 0);
       }
     } else {
 #pragma unroll
@@ -1118,11 +1136,14 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
     }
   } else {
     float v[S::kTaps];
-    if constexpr (STREAM) {
+    if constexpr (STREAM) {  // taps resolved and loaded in three groups (see k_stencil)
 #pragma unroll
-      for (int t = 0; t < S::kTaps; ++t) {
-        row[t] = side.row(resolve(t));
-        v[t] = side.load1(row[t], 0);
+      for (int grp = 0; grp < 3; ++grp) {
+        constexpr int kG = (S::kTaps + 2) / 3;
+#pragma unroll
+        for (int t = grp * kG; t < (grp + 1) * kG && t < S::kTaps; ++t) row[t] = side.row(resolve(t));
+#pragma unroll
+        for (int t = grp * kG; t < (grp + 1) * kG && t < S::kTaps; ++t) v[t] = side.load1(row[t], 0);
       }
     } else {
 #pragma unroll
