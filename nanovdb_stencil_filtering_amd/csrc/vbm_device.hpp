@@ -4,7 +4,8 @@
 // the same decode and resolvers (tests/custom_consumer.hip is one):
 //   device_grid_of         the device view of a grid (header + device blob)
 //   decode_slot            slot -> (leaf, voxel offset); thread-local, in registers
-//   resolve_tree           one tap by a root-down tree walk
+//   resolve_tree           one tap by a root-down tree walk (root table in
+//                          global memory, or in LDS after stage_root_table)
 //   stage_neighbour_table  per-block LDS table of neighbour leaf ids (all threads)
 //   stage_neighbour_records  the same table holding the neighbour leaves'
 //                          records (masks, prefix directory, first index), so
@@ -52,6 +53,7 @@ struct alignas(16) Leaf {  // 128 bytes: one cache line
   uint32_t pad[7];
 };
 static_assert(sizeof(Leaf) == 128, "leaf record");
+static_assert(offsetof(Leaf, prefix) == 64 && offsetof(Leaf, first) == 72, "prefix and first share a 16-byte piece");
 
 struct RootTile {
   int32_t key[3];
@@ -149,6 +151,25 @@ __device__ __forceinline__ uint32_t index_in_leaf(const R& L, uint32_t o) {
   const uint32_t rank = __popc(below) + (upper ? __popc(lo) : 0u);
   const uint32_t before = w ? prefix_field(L.prefix, w - 1) : 0u;
   const uint32_t idx = uint32_t(L.first) + before + rank;
+  return ((half >> sh) & 1u) ? idx : 0u;
+}
+
+// index_in_leaf of a Leaf record in global memory with the directory and the
+// first index read in one 16-byte load (they share the record's fifth 16-byte
+// piece), so the lookup is two loads from the record.  The tree walks with the
+// root table in LDS use this form; the arithmetic is index_in_leaf's.
+__device__ __forceinline__ uint32_t index_in_leaf_16(const Leaf& L, uint32_t o) {
+  const uint32_t w = o >> 6, b = o & 63;
+  const uint64_t m = L.mask[w];
+  const uint4 pf = *reinterpret_cast<const uint4*>(&L.prefix);  // prefix lo, prefix hi, first lo, first hi
+  const uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+  const bool upper = b >= 32;
+  const uint32_t half = upper ? hi : lo;
+  const uint32_t sh = b & 31;
+  const uint32_t below = __builtin_amdgcn_ubfe(half, 0, sh);
+  const uint32_t rank = __popc(below) + (upper ? __popc(lo) : 0u);
+  const uint32_t before = w ? prefix_field(uint64_t(pf.y) << 32 | pf.x, w - 1) : 0u;
+  const uint32_t idx = pf.z + before + rank;
   return ((half >> sh) & 1u) ? idx : 0u;
 }
 
@@ -253,6 +274,74 @@ __device__ __forceinline__ uint32_t resolve_tree(const DeviceGrid& g, int32_t x,
   const uint32_t leaf = find_leaf(g, x, y, z);
   if (leaf == kNoLeaf) return 0u;
   return index_in_leaf(g.leaves[leaf], (uint32_t(x) & 7) << 6 | (uint32_t(y) & 7) << 3 | (uint32_t(z) & 7));
+}
+
+// ---------------------------------------------------------------------------
+// root table in LDS
+// ---------------------------------------------------------------------------
+// The search over the root keys is the first and longest link of a walk's
+// chain of dependent loads (three or more steps before the upper node's
+// entry).  A kernel whose taps are tree walks copies a grid's root table into
+// LDS once per workgroup when it has at most kLdsRootTiles tiles, and its
+// walks search that copy; a grid with more tiles is searched in global memory.
+// The walk is the same root-down walk with the same answers either way.
+constexpr uint32_t kLdsRootTiles = 64;  // 1 KiB
+
+struct LdsRoot {
+  const RootTile* tiles;  // the workgroup's copy, in LDS (read only when staged)
+  bool staged;            // workgroup-uniform: g.n_root <= kLdsRootTiles
+};
+
+// Copies the root table into `lds` (room for kLdsRootTiles tiles, in LDS) if
+// it fits.  Every thread of the workgroup calls this before its first walk;
+// it ends with a barrier.
+__device__ __forceinline__ LdsRoot stage_root_table(const DeviceGrid& g, RootTile* lds) {
+  const bool staged = g.n_root <= kLdsRootTiles;
+  if (staged)
+    for (uint32_t i = threadIdx.x; i < g.n_root; i += blockDim.x) lds[i] = g.root[i];
+  __syncthreads();
+  return LdsRoot{lds, staged};
+}
+
+// Leaf containing voxel (x, y, z) below upper node `upper`: its upper-node
+// entry, then its lower-node entry; kNoLeaf if none (the steps of find_leaf
+// below the root).
+__device__ __forceinline__ uint32_t leaf_below(const DeviceGrid& g, uint32_t upper, int32_t x, int32_t y, int32_t z) {
+  const uint32_t uslot = ((uint32_t(x) >> 7) & 31) << 10 | ((uint32_t(y) >> 7) & 31) << 5 | ((uint32_t(z) >> 7) & 31);
+  const uint32_t lower = g.upper[uint64_t(upper) * 32768 + uslot];
+  if (lower == kNoLeaf) return kNoLeaf;
+  const uint32_t lslot = ((uint32_t(x) >> 3) & 15) << 8 | ((uint32_t(y) >> 3) & 15) << 4 | ((uint32_t(z) >> 3) & 15);
+  return g.lower[uint64_t(lower) * 4096 + lslot];
+}
+
+// resolve_tree with the root search over the LDS copy (the global one when not
+// staged), by halving steps from the largest power of two not above n_root (a
+// workgroup-uniform trip count): lo grows by `step` while the tile just below
+// lo + step is at or below the key, so it ends as the number of tiles at or
+// below (rx, ry, rz), and the last tile taken is the greatest of them: the
+// voxel's tile if it is equal to the key.  That tile's fields are kept as they
+// are read, so no read follows the search.
+__device__ __forceinline__ uint32_t resolve_tree(const DeviceGrid& g, const LdsRoot& r, int32_t x, int32_t y,
+                                                 int32_t z) {
+  if (!r.staged) return resolve_tree(g, x, y, z);
+  const int32_t rx = x >> 12, ry = y >> 12, rz = z >> 12;
+  const uint32_t n = g.n_root;
+  uint32_t lo = 0, upper = 0;
+  bool equal = false;
+  for (uint32_t step = n ? 1u << (31 - __builtin_clz(n)) : 0u; step; step >>= 1) {
+    if (lo + step <= n) {
+      const RootTile t = r.tiles[lo + step - 1];
+      if (!(rx < t.key[0] || (rx == t.key[0] && (ry < t.key[1] || (ry == t.key[1] && rz < t.key[2]))))) {
+        lo += step;
+        equal = t.key[0] == rx && t.key[1] == ry && t.key[2] == rz;
+        upper = t.upper;
+      }
+    }
+  }
+  if (!equal) return 0u;
+  const uint32_t leaf = leaf_below(g, upper, x, y, z);
+  if (leaf == kNoLeaf) return 0u;
+  return index_in_leaf_16(g.leaves[leaf], (uint32_t(x) & 7) << 6 | (uint32_t(y) & 7) << 3 | (uint32_t(z) & 7));
 }
 
 // Leaf at offset (8 dx, 8 dy, 8 dz) from leaf L (kNoLeaf if none), found
@@ -654,6 +743,13 @@ __device__ __forceinline__ void for_each_box(const DeviceGrid& g, Slot s, F&& f)
 }
 
 template <class F>
+__device__ __forceinline__ void for_each_box(const DeviceGrid& g, const LdsRoot& r, Slot s, F&& f) {
+  const VoxelCoord p = voxel_coord(g, s);
+#pragma unroll
+  for (int t = 0; t < kBoxTaps; ++t) f(t, resolve_tree(g, r, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+}
+
+template <class F>
 __device__ __forceinline__ void for_each_box_cached(const DeviceGrid& g, const uint32_t* table, uint32_t first_leaf,
                                                     Slot s, F&& f) {
   const uint32_t j = s.leaf - first_leaf;
@@ -664,6 +760,10 @@ __device__ __forceinline__ void for_each_box_cached(const DeviceGrid& g, const u
 
 __device__ __forceinline__ void compute_box(const DeviceGrid& g, Slot s, uint64_t (&st)[kBoxTaps]) {
   for_each_box(g, s, [&](int t, uint32_t idx) { st[t] = idx; });
+}
+
+__device__ __forceinline__ void compute_box(const DeviceGrid& g, const LdsRoot& r, Slot s, uint64_t (&st)[kBoxTaps]) {
+  for_each_box(g, r, s, [&](int t, uint32_t idx) { st[t] = idx; });
 }
 
 __device__ __forceinline__ void compute_box_cached(const DeviceGrid& g, const uint32_t* table, uint32_t first_leaf,
@@ -677,6 +777,13 @@ __device__ __forceinline__ void for_each_tap(const DeviceGrid& g, Slot s, F&& f)
   const VoxelCoord p = voxel_coord(g, s);
 #pragma unroll
   for (int t = 0; t < S::kTaps; ++t) f(t, resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+}
+
+template <class S, class F>
+__device__ __forceinline__ void for_each_tap(const DeviceGrid& g, const LdsRoot& r, Slot s, F&& f) {
+  const VoxelCoord p = voxel_coord(g, s);
+#pragma unroll
+  for (int t = 0; t < S::kTaps; ++t) f(t, resolve_tree(g, r, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
 }
 
 // Any shape: taps through the staged table of neighbour leaves (S::kDirs per

@@ -473,6 +473,7 @@ __global__ void __launch_bounds__(512) k_taps_box_cached(DeviceGrid g, uint64_t*
 template <class S, bool CACHED, bool STREAM>
 __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict__ taps) {
   __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];                // the plain resolver's root table
   const uint32_t b = blockIdx.x;
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
@@ -487,6 +488,9 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
       cached = true;
     }
   }
+  // the plain resolver's walks search the root table in LDS; the cached one's
+  // fallback walks (blocks spanning more than kMaxCachedLeaves) the global table
+  const LdsRoot root = CACHED ? LdsRoot{root_lds, false} : stage_root_table(g, root_lds);
   if (!valid) {
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) out[j] = 0;
@@ -495,12 +499,12 @@ __global__ void __launch_bounds__(512) k_taps(DeviceGrid g, uint64_t* __restrict
   if constexpr (STREAM) {
     auto put = [&](int t, uint32_t idx) { out[t] = idx; };
     if (cached) for_each_tap_staged<S>(staged, first, s, put);
-    else for_each_tap<S>(g, s, put);
+    else for_each_tap<S>(g, root, s, put);
   } else {
     uint64_t st[S::kTaps];
     auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
     if (cached) for_each_tap_staged<S>(staged, first, s, keep);
-    else for_each_tap<S>(g, s, keep);
+    else for_each_tap<S>(g, root, s, keep);
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) out[j] = st[j];
   }
@@ -511,8 +515,10 @@ template <int CH, bool VEC, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                    float* __restrict__ out, uint32_t C, uint32_t ch0) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
+  __shared__ RootTile root_lds[kLdsRootTiles];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
+  const LdsRoot root = stage_root_table(g, root_lds);
   const Slot s = decode_own_slot(g, b);
   if (s.leaf == kSentinelLeaf) return;
   const SC side = SC::make(sc, sc_bytes, C, ch0);
@@ -531,13 +537,13 @@ __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const int t = 9 * grp + k;
-        off[k] = side.tap(resolve_tree(g, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
+        off[k] = side.tap(resolve_tree(g, root, p.x + box_di(t), p.y + box_dj(t), p.z + box_dk(t)));
       }
       gather_box_pipelined<CH, VEC, kPipe, 9>(acc, side, [&](int k) { return off[k]; });
     }
   } else {
     uint64_t st[kBoxTaps];
-    compute_box(g, s, st);
+    compute_box(g, root, s, st);
     gather_box_pipelined<CH, VEC, kPipe>(acc, side, [&](int t) { return side.tap(uint32_t(st[t])); });
   }
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;
@@ -742,6 +748,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
                                                  float* __restrict__ out, uint32_t C, uint32_t ch0) {
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
   __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];                // the plain resolver's root table
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
@@ -756,6 +763,9 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
       cached = true;
     }
   }
+  // the plain resolver's walks search the root table in LDS; the cached one's
+  // fallback walks (blocks spanning more than kMaxCachedLeaves) the global table
+  const LdsRoot root = CACHED ? LdsRoot{root_lds, false} : stage_root_table(g, root_lds);
   const SC side = SC::make(sc, sc_bytes, C, ch0);
   // Rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks later (blocks go
   // round-robin over the 8 XCDs here, hence the factor 8).  Measured on MI355X:
@@ -795,7 +805,8 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
         for (int k = 0; k < N; ++k) {
           const int t = F + k;
           off[k] = (LAP && t == S::kCentre) ? side.inactive()
-                                            : side.tap(resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t)));
+                                            : side.tap(resolve_tree(g, root, p.x + S::di(t), p.y + S::dj(t),
+                                                                    p.z + S::dk(t)));
         }
         gather_box_pipelined<CH, VEC, (kPipe < N ? kPipe : N), N>(acc, side, [&](int k) { return off[k]; });
       };
@@ -807,7 +818,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
     uint64_t st[S::kTaps];
     auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
     if (cached) for_each_tap_staged<S>(staged, first, s, keep);
-    else for_each_tap<S>(g, s, keep);
+    else for_each_tap<S>(g, root, s, keep);
 #pragma unroll
     for (int j = 0; j < S::kTaps; ++j) {
       if (LAP && j == S::kCentre) continue;
@@ -843,6 +854,7 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
   constexpr uint32_t LANES = CH / 4;
   constexpr int kPipe = VBM_PIPE_SPLIT < S::kTaps ? VBM_PIPE_SPLIT : S::kTaps;
   __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];                // the plain resolver's root table
   __shared__ uint32_t slot_info[512];  // per slot: leaf-in-block << 16 | voxel offset, or 0xFFFFFFFF
   const uint32_t W = 1u << g.log2w;
   const uint32_t b = block_of_workgroup(blockIdx.x, g.n_blocks);
@@ -856,7 +868,11 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
     const Slot s = decode_own_slot(g, b);
     slot_info[threadIdx.x] = s.leaf == kSentinelLeaf ? 0xFFFFFFFFu : ((s.leaf - first) << 16) | s.offset;
   }
-  if (cached) stage_neighbour_records<S::kDirs>(g, first, span, staged);  // ends with a barrier
+  // either ends with a barrier (the slot table is read across the workgroup);
+  // the cached resolver's fallback walks search the global root table
+  LdsRoot root{root_lds, false};
+  if (!CACHED) root = stage_root_table(g, root_lds);
+  else if (cached) stage_neighbour_records<S::kDirs>(g, first, span, staged);
   else __syncthreads();
   // The rows of the block this XCD starts VBM_PREFETCH_AHEAD blocks later, into
   // the L2 (as in the split box kernel).  Measured on MI355X: 7-9 % faster for
@@ -882,7 +898,7 @@ __global__ void __launch_bounds__(512) k_stencil_split(DeviceGrid g, const float
       if (LAP && t == S::kCentre) return 0u;
       if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, di, dj, dk);
       const Leaf& L = g.leaves[first + j];
-      return resolve_tree(g, L.origin[0] + x + di, L.origin[1] + y + dj, L.origin[2] + z + dk);
+      return resolve_tree(g, root, L.origin[0] + x + di, L.origin[1] + y + dj, L.origin[2] + z + dk);
     });
     auto tap = [&](int t) -> uint32_t { return taps(t); };
     // bytes 16 q .. 16 q + 15 of each tap's row
@@ -1052,6 +1068,7 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
                                               float* __restrict__ out, uint32_t C) {
   using S = AxisShape;
   __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
+  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];                // the plain resolver's root table
   const uint32_t b = blockIdx.x;
   if (blockIdx.x == 0)
     for (uint32_t c = threadIdx.x; c < C; c += blockDim.x) out[c] = 0.0f;  // row 0
@@ -1067,6 +1084,9 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
       cached = true;
     }
   }
+  // the plain resolver's walks search the root table in LDS; the cached one's
+  // fallback walks (blocks spanning more than kMaxCachedLeaves) the global table
+  const LdsRoot root = CACHED ? LdsRoot{root_lds, false} : stage_root_table(g, root_lds);
   if (!valid) return;
   const SC side = SC::make(sc, sc_bytes, C, 0);
   const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
@@ -1075,7 +1095,7 @@ __global__ void __launch_bounds__(512) k_weno(DeviceGrid g, const float* __restr
   if (!cached) p = voxel_coord(g, s);
   auto resolve = [&](int t) -> uint32_t {
     if (cached) return resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t));
-    return resolve_tree(g, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t));
+    return resolve_tree(g, root, p.x + S::di(t), p.y + S::dj(t), p.z + S::dk(t));
   };
   uint32_t row[S::kTaps];  // handle of each tap's row (index 0: row 0, the background)
   const uint64_t idx = 1 + (uint64_t(b) << g.log2w) + threadIdx.x;

@@ -5,6 +5,7 @@ filters preserve the tap order and the fp32 add order of the oracle, so their
 outputs must match bit for bit as well (compared as uint32 patterns); the
 1e-6 relative tolerance of the target is therefore never needed here.
 """
+import itertools
 import sys
 
 import numpy as np
@@ -34,7 +35,33 @@ def hand_coords():
                      [0, 0, 8], [128, 0, 0], [0, -1, 0], [0, 0, -8], [7, 0, 0]], np.int32)
 
 
+def corner_blobs(n_corners, sparse=False, extra_tile=False):
+    """Blobs centred on root-tile corners (multiples of 4096) two tiles apart:
+    each blob straddles 8 root tiles, so n corners make 8 n tiles, one more with
+    extra_tile (a blob inside a single tile).  A blob is a random 14^3 patch at
+    density 0.3, or (sparse) one voxel in each leaf of a 4^3-leaf patch, so that
+    every block spans more than MaxCachedLeaves leaves.  The filters' tree walks
+    search the root table in LDS up to 64 tiles and in global memory beyond."""
+    corners = list(itertools.product(range(-2, 3), repeat=3))[:n_corners]  # x tiles -5 and -4 for n <= 25
+    parts = []
+    for i, (a, b, c) in enumerate(corners):
+        o = 8192 * np.array([a, b, c], np.int64)
+        if sparse:
+            parts.append(I.one_per_cell_coords(40 + i, 4).astype(np.int64) + (o - 16))
+        else:
+            parts.append(I.random_sparse_coords(40 + i, (14, 14, 14), 0.3, tuple(int(v) for v in o - 7)))
+    if extra_tile:
+        parts.append(I.random_sparse_coords(39, (6, 6, 6), 0.5, (100, 100, 20000)))  # root tile (0, 0, 4)
+    return np.concatenate([q.astype(np.int64) for q in parts]).astype(np.int32)
+
+
+ROOT_TILES = {"roots_64": 64, "roots_65": 65, "roots_sparse_64": 64, "roots_sparse_72": 72}
+
 GRIDS = {
+    "roots_64": lambda: corner_blobs(8),
+    "roots_65": lambda: corner_blobs(8, extra_tile=True),
+    "roots_sparse_64": lambda: corner_blobs(8, sparse=True),
+    "roots_sparse_72": lambda: corner_blobs(9, sparse=True),
     "hand": hand_coords,
     "tiny_shell": lambda: I.shell_coords(**I.TINY_SHELL),
     "straddle": lambda: I.random_sparse_coords(3, (18, 18, 18), 0.9, (4087, -9, -4100)),
@@ -100,7 +127,7 @@ BOX_FLAGS = [0, vbm.STREAMING, vbm.CACHED, vbm.CACHED | vbm.STREAMING]
 
 
 @pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube", "stress_small"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube", "stress_small", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_box_filter(name, C):
     # every BlockWidth: the brick capacity, the per-leaf x ranges and the number of
     # passes per block all depend on it; stress_small has blocks spanning from one
@@ -118,7 +145,7 @@ def test_box_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_cross_filter(name, C):
     for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
@@ -134,7 +161,7 @@ def test_cross_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_axis_filter(name, C):
     for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
@@ -149,7 +176,7 @@ def test_axis_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 4, 8])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_weno_filter(name, C):
     """WENO consumer: inactive taps read row 0, so row 0 holds a nonzero background
     here; C = 1 and 3 take the scalar kernel, 4 and 8 the float4 one."""
@@ -197,6 +224,20 @@ def test_constant_field_interior_is_27():
     vox = ref.voxels()
     interior = ((vox >= -7) & (vox <= 14)).all(axis=1)
     assert np.all(out[interior] == 13.5) and np.all(out[~interior] < 13.5)
+
+
+@pytest.mark.parametrize("name", sorted(ROOT_TILES))
+def test_root_tile_counts(name):
+    """The corner-blob grids have the root-tile counts their names promise (64:
+    the most the tree walks search in LDS; 65 and 72: searched in global memory),
+    and the sparse ones have blocks spanning more than MaxCachedLeaves leaves."""
+    g, _ = grid_pair(name, 6)
+    assert g.hdr.n_root == ROOT_TILES[name]
+    if "sparse" in name:
+        hdr, blob = vbm.build_host(GRIDS[name](), 6)
+        jump = vbm.blob_sections(hdr, blob)["block_jump"]
+        spans = 1 + np.array([sum(bin(int(w)).count("1") for w in row) for row in jump])
+        assert spans.min() > vbm.MAX_CACHED_LEAVES
 
 
 def test_fallback_grid_spans_more_than_16_leaves():
