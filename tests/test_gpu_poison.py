@@ -4,8 +4,9 @@ overwritten with a poison value before each brick pass) against the oracle.
 The box kernels build, per pass, only the x planes of each spanned leaf that
 the block's voxels reach, and leave the others as they were (from an earlier
 pass or an earlier workgroup on the CU).  With the poison, reading any cell the
-current pass did not build gives a wrong raw tap (0xFFFFFFFE) or adds the
-wrong row (row 1) -- a deterministic mismatch.  Grids and widths are chosen so
+current pass did not build gives a wrong raw tap (0xFFFFFFFE), adds the
+wrong row (row 1) or, in the value bricks of one-channel sidecars at W256 and
+W512, adds 1.0 -- a deterministic mismatch.  Grids and widths are chosen so
 that blocks span one to more than MaxCachedLeaves leaves, i.e. one pass,
 several passes per block, and the tree-walk fallback."""
 import os
