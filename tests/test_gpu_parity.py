@@ -285,6 +285,28 @@ def test_filters_on_unaligned_and_wide_buffers(C):
                 assert np.array_equal(u32(out), want[name].view(np.uint32)), (name, shift, flags)
 
 
+@pytest.mark.parametrize("name", ["tiny_shell", "stress_small", "hand", "roots_65"])
+def test_value_bricks_on_aligned_and_shifted_sidecars(name):
+    """One-channel sidecars at W256 and W512 take the value bricks: each brick
+    column reads its run of values with 16-byte loads at any 4-byte offset, and
+    the grid's last columns reach past the sidecar's end.  Sidecar and output
+    16-byte aligned and 4-byte aligned only, every row against the oracle."""
+    for log2w in (8, 9):
+        g, ref = grid_pair(name, log2w)
+        sc = I.sidecar(450, g.n_active, 1)
+        want = ref.box(sc).view(np.uint32)
+        n = sc.size
+        for shift in (0, 1, 2, 3):
+            big_in = torch.zeros(n + shift, dtype=torch.float32, device="cuda")
+            big_in[shift:] = torch.from_numpy(sc.ravel()).cuda()
+            sct = big_in[shift:].view(g.n_active + 1, 1)
+            for flags in (vbm.CACHED, vbm.CACHED | vbm.STREAMING):
+                say("value bricks %s W=%d shift=%d flags=%d" % (name, 1 << log2w, shift, flags))
+                out = torch.full_like(sct, float("nan"))
+                vbm.box_filter(g, sct, flags, out=out)
+                assert np.array_equal(u32(out), want), (log2w, shift, flags)
+
+
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
 @pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small"])
 def test_wide_rows_match_the_oracle(name, C):
