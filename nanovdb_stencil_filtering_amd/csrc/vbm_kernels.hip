@@ -814,24 +814,31 @@ __global__ void __launch_bounds__(1024) k_box_cached_split(DeviceGrid g, const f
 // Filters of the 7-direction shapes: the cross (sum, or 7-point Laplacian =
 // faces in cross order - fl(6 c)) and the 19-tap axis stencil (sum).  Taps by
 // tree walks or through the per-tap cached table; streamed into the gather
-// pipeline (STREAM) or materialised into an array first.
-template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM, class SC = Sidecar>
+// pipeline (STREAM) or materialised into an array first.  CAPL: spanned
+// leaves whose records are staged at a time; below kMaxCachedLeaves a block is
+// processed in passes of CAPL leaves (each voxel gathers in the pass holding
+// its leaf), so that LDS does not limit how many single-wave workgroups (W64)
+// are resident.
+template <class S, int CH, bool VEC, bool CACHED, bool LAP, bool STREAM, class SC = Sidecar,
+          int CAPL = kMaxCachedLeaves>
 __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                  float* __restrict__ out, uint32_t C, uint32_t ch0) {
+  static_assert(CAPL >= 1 && CAPL <= kMaxCachedLeaves, "records staged per pass");
+  constexpr bool kPasses = CAPL < kMaxCachedLeaves;
   constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
-  __shared__ StagedLeaf staged[CACHED ? kMaxCachedLeaves * S::kDirs : 1];  // neighbour leaf records
-  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];                // the plain resolver's root table
+  __shared__ StagedLeaf staged[CACHED ? CAPL * S::kDirs : 1];  // neighbour leaf records
+  __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];    // the plain resolver's root table
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
   const Slot s = decode_own_slot(g, b);
   const bool valid = s.leaf != kSentinelLeaf;
   bool cached = false;
-  uint32_t first = 0;
+  uint32_t first = 0, span = 0;
   if constexpr (CACHED) {
     first = g.block_first_leaf[b];
-    const uint32_t span = block_span(g, b);  // block-uniform: the barrier below is uniform
+    span = block_span(g, b);  // block-uniform: the barriers below are uniform
     if (span <= kMaxCachedLeaves) {
-      stage_neighbour_records<S::kDirs>(g, first, span, staged);
+      if constexpr (!kPasses) stage_neighbour_records<S::kDirs>(g, first, span, staged);
       cached = true;
     }
   }
@@ -847,22 +854,54 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
   if constexpr (kTouch)
     touch_block_lines(g, side, VBM_PREFETCH_AHEAD && b + 8 * VBM_PREFETCH_AHEAD < g.n_blocks
                                    ? b + 8 * VBM_PREFETCH_AHEAD : 0xFFFFFFFFu, ahead);
+  float acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+  if constexpr (CACHED && kPasses) {
+    // passes of CAPL spanned leaves: the records of leaves j0 .. j0 + count - 1
+    // in LDS, then the voxels of those leaves gather (the same taps, the same
+    // order as in one pass)
+    if (cached) {
+      const uint32_t j = valid ? s.leaf - first : 0xFFFFFFFFu;
+      const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+      for (uint32_t j0 = 0; j0 < span; j0 += CAPL) {
+        const uint32_t count = min(uint32_t(CAPL), span - j0);
+        if (j0) __syncthreads();  // the previous pass's records are no longer read
+        stage_neighbour_records<S::kDirs>(g, first + j0, count, staged);
+        if (j - j0 < count) {
+          if constexpr (STREAM) {
+            gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
+              if (LAP && t == S::kCentre) return side.inactive();
+              return side.tap(resolve_staged<S::kDirs>(staged, j - j0, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+            });
+          } else {
+            uint64_t st[S::kTaps];
+            for_each_tap_staged<S>(staged, first + j0, s, [&](int t, uint32_t idx) { st[t] = idx; });
+#pragma unroll
+            for (int t = 0; t < S::kTaps; ++t) {
+              if (LAP && t == S::kCentre) continue;
+              add_row<CH, VEC>(acc, side, side.tap(uint32_t(st[t])));
+            }
+          }
+        }
+      }
+    }
+  }
   if (!valid) {
     if constexpr (kTouch) consume_touch(ahead);
     return;
   }
-  float acc[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
   // the Laplacian's centre enters only as -6 * centre: it reads as an inactive tap here
   if constexpr (STREAM) {
     if (cached) {
-      const uint32_t j = s.leaf - first;
-      const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
-      gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
-        if (LAP && t == S::kCentre) return side.inactive();
-        return side.tap(resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
-      });
+      if constexpr (!kPasses) {
+        const uint32_t j = s.leaf - first;
+        const int x = int(s.offset >> 6), y = int((s.offset >> 3) & 7), z = int(s.offset & 7);
+        gather_box_pipelined<CH, VEC, kPipe, S::kTaps>(acc, side, [&](int t) {
+          if (LAP && t == S::kCentre) return side.inactive();
+          return side.tap(resolve_staged<S::kDirs>(staged, j, x, y, z, S::di(t), S::dj(t), S::dk(t)));
+        });
+      }
     } else {
       // tree walks streamed in three groups (as in the plain box): a group's walks
       // are independent chains of dependent loads that overlap one another, and
@@ -886,7 +925,7 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
       group(std::integral_constant<int, kG>{}, std::integral_constant<int, kG>{});
       group(std::integral_constant<int, 2 * kG>{}, std::integral_constant<int, S::kTaps - 2 * kG>{});
     }
-  } else {
+  } else if (!kPasses || !cached) {
     uint64_t st[S::kTaps];
     auto keep = [&](int t, uint32_t idx) { st[t] = idx; };
     if (cached) for_each_tap_staged<S>(staged, first, s, keep);
@@ -1441,7 +1480,10 @@ bool wide_rows(const vbm_grid* grid, int C, int flags) {
 }
 
 // Brick capacity (spanned leaves resolved per pass) for BlockWidth 2^log2w:
-// one pass covers about 98% of the blocks of a sphere shell.
+// one pass covers about 98% of the blocks of a sphere shell.  A W64 workgroup
+// is a single wave, so its LDS sets how many are resident: capacity 2 (8.3 KB)
+// keeps 19 per CU where 3 kept 12, measured 12-15 % faster on the shell at one
+// to four channels (capacity 1: more passes, a little slower than 2).
 #ifndef VBM_CAP_W128
 #define VBM_CAP_W128 3
 #endif
@@ -1449,21 +1491,23 @@ bool wide_rows(const vbm_grid* grid, int C, int flags) {
 #define VBM_CAP_W512 8
 #endif
 uint32_t brick_capacity(int log2w) {
-  return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_CAP_W128) : log2w == 8 ? 6u : uint32_t(VBM_CAP_W512);
+  return log2w <= 6 ? 2u : log2w == 7 ? uint32_t(VBM_CAP_W128) : log2w == 8 ? 6u : uint32_t(VBM_CAP_W512);
 }
 
 // Brick capacity of the split-row kernel, whose staged leaf records take
 // 27 * 80 bytes of LDS per spanned leaf on top of the brick: sized so that a
-// W128 workgroup still fits eight to a CU.
+// W128 workgroup still fits eight to a CU.  At W64 (workgroups of two waves at
+// 8 channels, four at 16) capacity 2 is 11 % faster than 3 at 8 channels and
+// 3 % slower at 16, measured on the shell.
 #ifndef VBM_SPLIT_CAP_W128
 #define VBM_SPLIT_CAP_W128 3
 #endif
 #ifndef VBM_SPLIT_CAP_W512
 #define VBM_SPLIT_CAP_W512 8
 #endif
-uint32_t split_capacity(int log2w) {
+uint32_t split_capacity(int log2w, int ch) {
   if (!VBM_STAGE_LEAVES) return brick_capacity(log2w);
-  return log2w <= 6 ? 3u : log2w == 7 ? uint32_t(VBM_SPLIT_CAP_W128) : log2w == 8 ? 4u : uint32_t(VBM_SPLIT_CAP_W512);
+  return log2w <= 6 ? (ch == 8 ? 2u : 3u) : log2w == 7 ? uint32_t(VBM_SPLIT_CAP_W128) : log2w == 8 ? 4u : uint32_t(VBM_SPLIT_CAP_W512);
 }
 
 template <bool CACHED, bool STREAM, bool WIDE = false>
@@ -1473,7 +1517,7 @@ struct BoxLauncher {
   static void go(const DeviceGrid& g, const float* sc, uint32_t bytes, float* out, uint32_t C, uint32_t ch0,
                  hipStream_t st) {
     if constexpr (WIDE && CACHED && VEC && (CH == 8 || CH == 16)) {  // rows by 64-bit addresses
-      const uint32_t cap = split_capacity(g.log2w);
+      const uint32_t cap = split_capacity(g.log2w, CH);
       const uint32_t W = 1u << g.log2w;
       const uint32_t tasks = W * (CH / 4);
       const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
@@ -1489,7 +1533,7 @@ struct BoxLauncher {
                            st, g, sc, bytes, out, C, ch0);
       }
     } else if constexpr (CACHED && VEC && (CH == 8 || CH == 16)) {
-      const uint32_t cap = split_capacity(g.log2w);
+      const uint32_t cap = split_capacity(g.log2w, CH);
       const uint32_t W = 1u << g.log2w;
       const uint32_t tasks = W * (CH / 4);
       const uint32_t threads = tasks < VBM_SPLIT_MAX ? tasks : (W > VBM_SPLIT_MAX ? W : VBM_SPLIT_MAX);
@@ -1540,6 +1584,19 @@ struct StencilLauncher {
       hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM, WideSidecar>), dim3(g.n_blocks),
                          dim3(1u << g.log2w), 0, st, g, sc, bytes, out, C, ch0);
     } else {
+      if constexpr (CACHED && S::kTaps == 7) {
+        if (g.log2w == 6) {
+          // single-wave workgroups: records staged four leaves at a time, so that
+          // LDS (2.2 KB instead of 8.75 KB) does not cap how many are resident.
+          // Measured on the shell: cross sum and Laplacian 13-17 % faster at one
+          // channel, 0-10 % at eight; the 19-tap axis stencil's pass loop needs
+          // 105 VGPRs instead of 56 at eight channels and is 5 % slower, so it
+          // keeps one pass
+          hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM, Sidecar, 4>), dim3(g.n_blocks), dim3(64), 0,
+                             st, g, sc, bytes, out, C, ch0);
+          return;
+        }
+      }
       hipLaunchKernelGGL((k_stencil<S, CH, VEC, CACHED, LAP, STREAM>), dim3(g.n_blocks), dim3(1u << g.log2w), 0, st,
                          g, sc, bytes, out, C, ch0);
     }
