@@ -68,6 +68,10 @@ GRIDS = {
     "dense_cube": lambda: I.random_sparse_coords(4, (24, 24, 24), 1.0, (-8, -8, -8)),
     "one_per_leaf": lambda: I.one_per_cell_coords(5, 12),       # every block spans > 16 leaves
     "stress_small": lambda: I.leaf_bernoulli_coords(4, 2000, 20, (0.02, 0.1, 0.5, 1.0)),
+    # leaves 1.5-6 % full: W64 blocks span 1-9 leaves (the W64 cross and Laplacian
+    # stage records four leaves per pass), W128 5-16 (several brick passes),
+    # W256 and W512 mostly more than MaxCachedLeaves
+    "sparse_leaves": lambda: I.leaf_bernoulli_coords(7, 800, 14, (0.015, 0.03, 0.06)),
 }
 
 _cache = {}
@@ -127,7 +131,7 @@ BOX_FLAGS = [0, vbm.STREAMING, vbm.CACHED, vbm.CACHED | vbm.STREAMING]
 
 
 @pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube", "stress_small", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "hand", "dense_cube", "stress_small", "sparse_leaves", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_box_filter(name, C):
     # every BlockWidth: the brick capacity, the per-leaf x ranges and the number of
     # passes per block all depend on it; stress_small has blocks spanning from one
@@ -145,7 +149,7 @@ def test_box_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "stress_small", "sparse_leaves", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_cross_filter(name, C):
     for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
@@ -161,7 +165,7 @@ def test_cross_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 8, 16, 20])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small", "sparse_leaves", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_axis_filter(name, C):
     for log2w in (6, 7, 8, 9):
         g, ref = grid_pair(name, log2w)
@@ -176,7 +180,7 @@ def test_axis_filter(name, C):
 
 
 @pytest.mark.parametrize("C", [1, 3, 4, 8])
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "one_per_leaf", "dense_cube", "hand", "stress_small", "sparse_leaves", "roots_64", "roots_65", "roots_sparse_64", "roots_sparse_72"])
 def test_weno_filter(name, C):
     """WENO consumer: inactive taps read row 0, so row 0 holds a nonzero background
     here; C = 1 and 3 take the scalar kernel, 4 and 8 the float4 one."""

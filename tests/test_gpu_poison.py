@@ -39,7 +39,8 @@ def test_poisoned_build_is_a_separate_library():
         assert a.read() != b.read()
 
 
-@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "dense_cube", "stress_small", "hand", "one_per_leaf"])
+@pytest.mark.parametrize("name", ["tiny_shell", "straddle", "dense_cube", "stress_small", "sparse_leaves", "hand",
+                                  "one_per_leaf"])
 def test_poisoned_bricks_match_the_oracle(name):
     coords = GRIDS[name]()
     ref = oracle.OracleGrid(coords)
