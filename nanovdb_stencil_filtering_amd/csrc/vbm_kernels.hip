@@ -288,7 +288,10 @@ __device__ __forceinline__ void consume_touch(const float (&v)[N]) {
 #define VBM_PIPE_WIDE 2   // taps in flight per work-item for CH >= 8
 #endif
 #ifndef VBM_PIPE_NARROW
-#define VBM_PIPE_NARROW 4  // taps in flight per work-item for CH < 8
+// taps in flight per work-item for CH < 8: 6 is 1-3 % faster than 4 on the
+// one- to four-channel box, cross, Laplacian and axis kernels (8: about the
+// same as 6, slower at 3 channels W512)
+#define VBM_PIPE_NARROW 6
 #endif
 #ifndef VBM_XCD_REMAP
 #define VBM_XCD_REMAP 1    // 1: give each of the 8 XCDs a contiguous range of blocks
@@ -566,7 +569,10 @@ __device__ __forceinline__ void build_value_bricks(const DeviceGrid& g, const ui
 template <int CH, bool VEC, bool STREAM, class SC = Sidecar>
 __global__ void __launch_bounds__(512) k_box_plain(DeviceGrid g, const float* __restrict__ sc, uint32_t sc_bytes,
                                                    float* __restrict__ out, uint32_t C, uint32_t ch0) {
-  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
+  // taps in flight per work-item; the materialised form holds all 27 taps as
+  // well, and at 3-4 channels six in flight would take it past 64 VGPRs (8 waves
+  // per SIMD): measured 2-7 % slower than four, so it keeps four
+  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : (STREAM || CH < 3 ? VBM_PIPE_NARROW : 4);
   __shared__ RootTile root_lds[kLdsRootTiles];
   const uint32_t b = blockIdx.x;
   zero_index_row<CH>(out, ch0);
