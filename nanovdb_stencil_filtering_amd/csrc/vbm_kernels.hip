@@ -831,7 +831,11 @@ __global__ void __launch_bounds__(512) k_stencil(DeviceGrid g, const float* __re
                                                  float* __restrict__ out, uint32_t C, uint32_t ch0) {
   static_assert(CAPL >= 1 && CAPL <= kMaxCachedLeaves, "records staged per pass");
   constexpr bool kPasses = CAPL < kMaxCachedLeaves;
-  constexpr int kPipe = CH >= 8 ? VBM_PIPE_WIDE : VBM_PIPE_NARROW;  // taps in flight per work-item
+  // taps in flight per work-item; the streamed form at eight or more channels
+  // takes a deeper pipeline than the box's two (measured on the shell, cached
+  // streamed C=8: cross 1-2 % faster with three, 19-tap axis 1-7 % with four)
+  constexpr int kPipe =
+      CH >= 8 ? (STREAM ? (S::kTaps > 7 ? 4 : 3) : VBM_PIPE_WIDE) : VBM_PIPE_NARROW;
   __shared__ StagedLeaf staged[CACHED ? CAPL * S::kDirs : 1];  // neighbour leaf records
   __shared__ RootTile root_lds[CACHED ? 1 : kLdsRootTiles];    // the plain resolver's root table
   const uint32_t b = blockIdx.x;
